@@ -1,0 +1,43 @@
+"""Float64 CPU oracle for the SAF hybrid attention layer -- TEST INFRASTRUCTURE.
+
+This package is a plain, slow, dense implementation of what the layer
+computes, written from "When Can Attention Heads Be Statically Defined?"
+(Section 3, Section 3.2 Equation 3, Appendix A.1 Equations 5-7, Appendix D.2).
+It exists only to check the HIP library.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import it; the library and its Python binding never do, and nothing here
+imports them.
+
+Every function is pinned by a CPU test to something other than itself
+(closed forms, a hand-worked example, library routines, finite differences).
+"""
+
+from .saf_oracle import (
+    frozen_head_bwd,
+    frozen_head_fwd,
+    frozen_logits,
+    frozen_lognorm,
+    frozen_pattern,
+    frozen_rows_fwd,
+    hybrid_bwd,
+    hybrid_fwd,
+    ordinary_head_bwd,
+    ordinary_head_fwd,
+    ordinary_rows_fwd,
+    default_scale,
+)
+
+__all__ = [
+    "frozen_head_bwd",
+    "frozen_head_fwd",
+    "frozen_logits",
+    "frozen_lognorm",
+    "frozen_pattern",
+    "frozen_rows_fwd",
+    "hybrid_bwd",
+    "hybrid_fwd",
+    "ordinary_head_bwd",
+    "ordinary_head_fwd",
+    "ordinary_rows_fwd",
+    "default_scale",
+]
