@@ -1,0 +1,249 @@
+"""ctypes binding of libsaf_hybrid.so (argument marshalling only).
+
+Every computation runs in the HIP library; this module only turns torch
+tensors into pointers, strides and a parameter block, allocates outputs and
+the workspace with torch, and raises on a non-zero status.  If the library is
+missing, importing this module raises -- there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsaf_hybrid.so")
+
+SAF_OK = 0
+SAF_EINVAL = -1
+SAF_EUNSUPPORTED = -2
+SAF_EWORKSPACE = -3
+SAF_EHIP = -4
+SAF_F32 = 0
+SAF_BF16 = 1
+
+EXPORTED = (
+    "saf_hybrid_attn_fwd",
+    "saf_hybrid_attn_bwd",
+    "saf_hybrid_attn_workspace_bytes",
+    "saf_pattern_dense",
+    "saf_pattern_lognorm",
+    "saf_status_string",
+    "saf_version",
+)
+
+_i64x3 = ctypes.c_int64 * 3
+
+
+class SafParams(ctypes.Structure):
+    """Mirror of ``saf_attn_params`` in include/saf_hybrid.h."""
+
+    _fields_ = [
+        ("struct_bytes", ctypes.c_uint32),
+        ("B", ctypes.c_int32),
+        ("H", ctypes.c_int32),
+        ("T", ctypes.c_int32),
+        ("D", ctypes.c_int32),
+        ("prior_len", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("q_stride", _i64x3),
+        ("k_stride", _i64x3),
+        ("v_stride", _i64x3),
+        ("o_stride", _i64x3),
+        ("do_stride", _i64x3),
+        ("dq_stride", _i64x3),
+        ("dk_stride", _i64x3),
+        ("dv_stride", _i64x3),
+        ("frozen", ctypes.POINTER(ctypes.c_uint8)),
+        ("stage_events", ctypes.c_void_p),
+        ("n_stage_events", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
+    ]
+
+
+class SafError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m fixed_pattern_hybrid_amd.build` "
+            "(the HIP library is required; there is no CPU fallback)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    pp = ctypes.POINTER(SafParams)
+    lib.saf_hybrid_attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_hybrid_attn_fwd.restype = ctypes.c_int
+    lib.saf_hybrid_attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_hybrid_attn_bwd.restype = ctypes.c_int
+    lib.saf_hybrid_attn_workspace_bytes.argtypes = [pp, ctypes.c_int]
+    lib.saf_hybrid_attn_workspace_bytes.restype = sz
+    lib.saf_pattern_dense.argtypes = [i32, i32, vp, vp, vp, vp]
+    lib.saf_pattern_dense.restype = ctypes.c_int
+    lib.saf_pattern_lognorm.argtypes = [i32, i32, i32, vp, vp, vp, vp]
+    lib.saf_pattern_lognorm.restype = ctypes.c_int
+    lib.saf_status_string.argtypes = [ctypes.c_int]
+    lib.saf_status_string.restype = ctypes.c_char_p
+    lib.saf_version.argtypes = []
+    lib.saf_version.restype = ctypes.c_int32
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.saf_status_string(int(status)).decode()
+
+
+def version() -> Tuple[int, int]:
+    v = LIB.saf_version()
+    return (v >> 16, v & 0xFFFF)
+
+
+def _check(status: int, what: str) -> None:
+    if status != SAF_OK:
+        raise SafError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stride3(t: Optional[torch.Tensor]):
+    if t is None:
+        return _i64x3(0, 0, 0)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("expected a [B, H, T, D] tensor with unit stride on D")
+    return _i64x3(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SAF_BF16
+    if t.dtype == torch.float32:
+        return SAF_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+class Params:
+    """Owns a SafParams block and the host arrays it points to."""
+
+    def __init__(self, v: torch.Tensor, frozen: Sequence[int], prior_len: int,
+                 softmax_scale: Optional[float] = None, events=None):
+        B, H, T, D = v.shape
+        self.frozen_arr = (ctypes.c_uint8 * H)(*[int(x) for x in frozen])
+        if len(frozen) != H:
+            raise ValueError("frozen mask needs one entry per head")
+        self.p = SafParams()
+        self.p.struct_bytes = ctypes.sizeof(SafParams)
+        self.p.B, self.p.H, self.p.T, self.p.D = B, H, T, D
+        self.p.prior_len = int(prior_len)
+        self.p.dtype = _dtype_code(v)
+        self.p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
+        self.p.frozen = ctypes.cast(self.frozen_arr, ctypes.POINTER(ctypes.c_uint8))
+        self.events_arr = None
+        if events:
+            handles = [int(e.cuda_event) for e in events]
+            self.events_arr = (ctypes.c_void_p * len(handles))(*handles)
+            self.p.stage_events = ctypes.cast(self.events_arr, ctypes.c_void_p)
+            self.p.n_stage_events = len(handles)
+
+    def set_strides(self, **tensors):
+        for name, t in tensors.items():
+            setattr(self.p, name + "_stride", _stride3(t))
+
+    def ref(self):
+        return ctypes.byref(self.p)
+
+
+def workspace_bytes(params: Params, for_bwd: bool) -> int:
+    return int(LIB.saf_hybrid_attn_workspace_bytes(params.ref(), 1 if for_bwd else 0))
+
+
+def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse=None,
+                        stream=None, events=None):
+    """Forward of the hybrid layer; returns (O, lse).
+
+    q, k, v: [B, H, T, D] bf16 or fp32 CUDA tensors (unit stride on D);
+    frozen: length-H sequence of 0/1; a, r: fp32 [H, Tp] contiguous.
+    """
+    B, H, T, D = v.shape
+    if a.dtype != torch.float32 or r.dtype != torch.float32 or not a.is_contiguous() or not r.is_contiguous():
+        raise ValueError("a and r must be contiguous float32 [H, Tp]")
+    if a.shape != r.shape or a.shape[0] != H:
+        raise ValueError("a and r must both be [H, Tp]")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    prm = Params(v, frozen, a.shape[1], softmax_scale, events)
+    prm.set_strides(q=q, k=k, v=v, o=out)
+    ws_n = workspace_bytes(prm, False)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
+    st = LIB.saf_hybrid_attn_fwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(r), _ptr(out),
+                                 _ptr(lse), _ptr(ws), ws_n, _stream_handle(stream))
+    _check(st, "saf_hybrid_attn_fwd")
+    return out, lse
+
+
+def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
+                        dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
+    """Backward of the hybrid layer; returns (dQ, dK, dV)."""
+    B, H, T, D = v.shape
+    if a.dtype != torch.float32 or r.dtype != torch.float32 or not a.is_contiguous() or not r.is_contiguous():
+        raise ValueError("a and r must be contiguous float32 [H, Tp]")
+    if not lse.is_contiguous() or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+        raise ValueError("lse must be contiguous float32 [B, H, T]")
+    mk = lambda: torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)  # noqa: E731
+    dq = mk() if dq is None else dq
+    dk = mk() if dk is None else dk
+    dv = mk() if dv is None else dv
+    prm = Params(v, frozen, a.shape[1], softmax_scale, events)
+    prm.set_strides(q=q, k=k, v=v, o=o, do=dout, dq=dq, dk=dk, dv=dv)
+    ws_n = workspace_bytes(prm, True)
+    if workspace is None:
+        workspace = torch.empty(ws_n, dtype=torch.uint8, device=v.device)
+    st = LIB.saf_hybrid_attn_bwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                 _ptr(a), _ptr(r), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 workspace.numel(), _stream_handle(stream))
+    _check(st, "saf_hybrid_attn_bwd")
+    return dq, dk, dv
+
+
+def saf_pattern_dense(a_h: torch.Tensor, r_h: torch.Tensor, T: int, stream=None) -> torch.Tensor:
+    """Dense [T, T] fp32 compact pattern of one frozen head."""
+    if a_h.dtype != torch.float32 or r_h.dtype != torch.float32:
+        raise ValueError("a and r must be float32")
+    Tp = min(a_h.numel(), r_h.numel())
+    w = torch.empty((T, T), dtype=torch.float32, device=a_h.device)
+    _check(LIB.saf_pattern_dense(T, Tp, _ptr(a_h), _ptr(r_h), _ptr(w), _stream_handle(stream)),
+           "saf_pattern_dense")
+    return w
+
+
+def saf_pattern_lognorm(a: torch.Tensor, r: torch.Tensor, T: int, stream=None) -> torch.Tensor:
+    """log N(i) for every row of a, r ([n, Tp] fp32): returns [n, T]."""
+    if a.dtype != torch.float32 or r.dtype != torch.float32 or a.shape != r.shape:
+        raise ValueError("a and r must be float32 [n, Tp]")
+    a = a.contiguous()
+    r = r.contiguous()
+    n, Tp = a.shape
+    out = torch.empty((n, T), dtype=torch.float32, device=a.device)
+    _check(LIB.saf_pattern_lognorm(n, T, Tp, _ptr(a), _ptr(r), _ptr(out), _stream_handle(stream)),
+           "saf_pattern_lognorm")
+    return out

@@ -1,0 +1,287 @@
+// C ABI of the SAF hybrid attention library: argument validation, head
+// lists, workspace accounting and kernel sequencing.  Every check runs on the
+// host before anything is enqueued.
+#include "saf_hybrid.h"
+#include "saf_internal.h"
+
+#include <cmath>
+#include <cstring>
+
+namespace saf {
+hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
+}
+
+namespace {
+
+using saf::BwdArgs;
+using saf::FwdArgs;
+using saf::LognormArgs;
+using saf::TensorRef;
+
+constexpr int32_t kVersion = (1 << 16) | 0;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == SAF_BF16 ? 2 : 4; }
+
+bool supported_d(int dtype, int D) {
+  if (dtype == SAF_BF16) return D == 64 || D == 96 || D == 128;
+  if (dtype == SAF_F32) return D == 16 || D == 32 || D == 64 || D == 96 || D == 128;
+  return false;
+}
+
+// Common shape checks; counts heads of each kind.
+int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
+  if (!p) return SAF_EINVAL;
+  if (p->struct_bytes != sizeof(saf_attn_params)) return SAF_EINVAL;
+  if (p->reserved1 != 0) return SAF_EINVAL;
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->D < 1) return SAF_EINVAL;
+  if (p->T > SAF_MAX_T) return SAF_EUNSUPPORTED;
+  if (p->H > SAF_MAX_HEADS) return SAF_EUNSUPPORTED;
+  if (p->B > 65535) return SAF_EUNSUPPORTED;
+  if (p->prior_len < p->T) return SAF_EINVAL;
+  if (p->dtype != SAF_F32 && p->dtype != SAF_BF16) return SAF_EUNSUPPORTED;
+  if (!supported_d(p->dtype, p->D)) return SAF_EUNSUPPORTED;
+  if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return SAF_EINVAL;
+  if (!p->frozen) return SAF_EINVAL;
+  if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return SAF_EINVAL;
+  int o = 0, f = 0;
+  for (int h = 0; h < p->H; ++h) {
+    if (p->frozen[h] == 1) ++f;
+    else if (p->frozen[h] == 0) ++o;
+    else return SAF_EINVAL;
+  }
+  *n_ord = o;
+  *n_frz = f;
+  // every (b, h, t) offset and B*H*T must fit comfortably in int64 / grids
+  if ((int64_t)p->B * p->H * p->T > (int64_t)1 << 40) return SAF_EUNSUPPORTED;
+  return SAF_OK;
+}
+
+int check_tensor(const void* ptr, const int64_t* s, const saf_attn_params* p) {
+  if (!ptr) return SAF_EINVAL;
+  if (!aligned(ptr, 16)) return SAF_EINVAL;
+  const size_t eb = elem_bytes(p->dtype);
+  const int64_t vec = (int64_t)(16 / eb);  // elements per 16 bytes
+  for (int x = 0; x < 3; ++x) {
+    if (s[x] < 0) return SAF_EINVAL;
+    if (s[x] % vec != 0) return SAF_EINVAL;
+  }
+  if (p->T > 1 && s[2] < p->D) return SAF_EINVAL;  // rows of one head may not overlap
+  return SAF_OK;
+}
+
+TensorRef ref(const void* ptr, const int64_t* s) {
+  TensorRef t;
+  t.ptr = const_cast<void*>(ptr);
+  t.sb = s[0];
+  t.sh = s[1];
+  t.st = s[2];
+  return t;
+}
+
+float resolve_scale(const saf_attn_params* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / std::sqrt((float)p->D);
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t bwd_ws_bytes(const saf_attn_params* p) {
+  return round_up((size_t)p->B * p->H * p->T * sizeof(float), 256);
+}
+
+// Records stage event k when the caller asked for it.
+struct Stages {
+  const saf_attn_params* p;
+  hipStream_t s;
+  int next = 0;
+  hipError_t mark() {
+    if (p->stage_events && next < p->n_stage_events) {
+      hipError_t e = hipEventRecord(p->stage_events[next], s);
+      ++next;
+      return e;
+    }
+    ++next;
+    return hipSuccess;
+  }
+};
+
+void fill_heads(const saf_attn_params* p, uint8_t* ord, uint8_t* frz, uint8_t* isf) {
+  int o = 0, f = 0;
+  for (int h = 0; h < p->H; ++h) {
+    if (isf) isf[h] = p->frozen[h];
+    if (p->frozen[h]) frz[f++] = (uint8_t)h;
+    else ord[o++] = (uint8_t)h;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* saf_status_string(int status) {
+  switch (status) {
+    case SAF_OK: return "ok";
+    case SAF_EINVAL: return "invalid argument (pointer, size, stride or alignment)";
+    case SAF_EUNSUPPORTED: return "unsupported configuration (head dim, dtype or size)";
+    case SAF_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SAF_EHIP: return "HIP runtime or launch failure";
+    default: return "unknown status";
+  }
+}
+
+int32_t saf_version(void) { return kVersion; }
+
+size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd) {
+  int o, f;
+  if (check_params(p, &o, &f) != SAF_OK) return 0;
+  return for_bwd ? bwd_ws_bytes(p) : 0;
+}
+
+int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
+                        const float* a, const float* r, void* o, float* lse, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;  // the forward needs no workspace
+  int n_ord = 0, n_frz = 0;
+  int st = check_params(p, &n_ord, &n_frz);
+  if (st != SAF_OK) return st;
+  if (n_ord > 0) {
+    if ((st = check_tensor(q, p->q_stride, p)) != SAF_OK) return st;
+    if ((st = check_tensor(k, p->k_stride, p)) != SAF_OK) return st;
+  }
+  if ((st = check_tensor(v, p->v_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
+  if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
+  if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
+
+  FwdArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.q = ref(q, p->q_stride);
+  args.k = ref(k, p->k_stride);
+  args.v = ref(v, p->v_stride);
+  args.o = ref(o, p->o_stride);
+  args.a = a;
+  args.r = r;
+  args.lse = lse;
+  args.B = p->B;
+  args.H = p->H;
+  args.T = p->T;
+  args.prior_len = p->prior_len;
+  args.scale_log2 = resolve_scale(p) * 1.4426950408889634f;
+  args.n_ord = n_ord;
+  args.n_frz = n_frz;
+  fill_heads(p, args.ord_heads, args.frz_heads, nullptr);
+
+  Stages stg{p, stream};
+  if (stg.mark() != hipSuccess) return SAF_EHIP;
+  if (n_frz > 0) {
+    LognormArgs la;
+    std::memset(&la, 0, sizeof(la));
+    la.a = a;
+    la.r = r;
+    la.out = lse;
+    la.out_b_stride = (int64_t)p->H * p->T;
+    la.out_h_stride = p->T;
+    la.n_heads = n_frz;
+    la.B = p->B;
+    la.T = p->T;
+    la.prior_len = p->prior_len;
+    std::memcpy(la.heads, args.frz_heads, sizeof(la.heads));
+    if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;
+    if (stg.mark() != hipSuccess) return SAF_EHIP;
+  }
+  hipError_t e = (p->dtype == SAF_BF16) ? saf::launch_fwd_bf16(args, p->D, stream)
+                                        : saf::launch_fwd_f32(args, p->D, stream);
+  if (e != hipSuccess) return SAF_EHIP;
+  if (stg.mark() != hipSuccess) return SAF_EHIP;
+  return SAF_OK;
+}
+
+int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse, const float* a,
+                        const float* r, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  int n_ord = 0, n_frz = 0;
+  int st = check_params(p, &n_ord, &n_frz);
+  if (st != SAF_OK) return st;
+  if (n_ord > 0) {
+    if ((st = check_tensor(q, p->q_stride, p)) != SAF_OK) return st;
+    if ((st = check_tensor(k, p->k_stride, p)) != SAF_OK) return st;
+    if ((st = check_tensor(v, p->v_stride, p)) != SAF_OK) return st;
+    if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
+  }
+  if ((st = check_tensor(dout, p->do_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(dq, p->dq_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(dk, p->dk_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(dv, p->dv_stride, p)) != SAF_OK) return st;
+  if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
+  if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
+  const size_t need = bwd_ws_bytes(p);
+  if (!ws || ws_bytes < need || !aligned(ws, 256)) return SAF_EWORKSPACE;
+
+  BwdArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.q = ref(q, p->q_stride);
+  args.k = ref(k, p->k_stride);
+  args.v = ref(v, p->v_stride);
+  args.o = ref(o, p->o_stride);
+  args.dout = ref(dout, p->do_stride);
+  args.dq = ref(dq, p->dq_stride);
+  args.dk = ref(dk, p->dk_stride);
+  args.dv = ref(dv, p->dv_stride);
+  args.a = a;
+  args.r = r;
+  args.lse = lse;
+  args.delta = static_cast<float*>(ws);
+  args.B = p->B;
+  args.H = p->H;
+  args.T = p->T;
+  args.prior_len = p->prior_len;
+  args.scale = resolve_scale(p);
+  args.scale_log2 = args.scale * 1.4426950408889634f;
+  args.n_ord = n_ord;
+  args.n_frz = n_frz;
+  fill_heads(p, args.ord_heads, args.frz_heads, args.is_frozen);
+
+  const bool bf = p->dtype == SAF_BF16;
+  Stages stg{p, stream};
+  if (stg.mark() != hipSuccess) return SAF_EHIP;
+  hipError_t e = bf ? saf::launch_bwd_pre_bf16(args, p->D, stream)
+                    : saf::launch_bwd_pre_f32(args, p->D, stream);
+  if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+  e = bf ? saf::launch_bwd_kv_bf16(args, p->D, stream) : saf::launch_bwd_kv_f32(args, p->D, stream);
+  if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+  if (n_ord > 0) {
+    e = bf ? saf::launch_bwd_q_bf16(args, p->D, stream) : saf::launch_bwd_q_f32(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+  }
+  return SAF_OK;
+}
+
+int saf_pattern_dense(int32_t T, int32_t prior_len, const float* a, const float* r, float* w,
+                      hipStream_t stream) {
+  if (T < 1 || T > 32768 || prior_len < T) return SAF_EINVAL;
+  if (!a || !r || !w || !aligned(a, 4) || !aligned(r, 4) || !aligned(w, 4)) return SAF_EINVAL;
+  return saf::launch_pattern_dense(T, prior_len, a, r, w, stream) == hipSuccess ? SAF_OK : SAF_EHIP;
+}
+
+int saf_pattern_lognorm(int32_t n_heads, int32_t T, int32_t prior_len, const float* a,
+                        const float* r, float* logz, hipStream_t stream) {
+  if (n_heads < 1 || n_heads > 65535 || T < 1 || T > SAF_MAX_T || prior_len < T) return SAF_EINVAL;
+  if (!a || !r || !logz || !aligned(a, 4) || !aligned(r, 4) || !aligned(logz, 4)) return SAF_EINVAL;
+  LognormArgs la;
+  std::memset(&la, 0, sizeof(la));
+  la.a = a;
+  la.r = r;
+  la.out = logz;
+  la.out_b_stride = 0;
+  la.out_h_stride = T;
+  la.n_heads = n_heads;
+  la.B = 1;
+  la.T = T;
+  la.prior_len = prior_len;
+  return saf::launch_lognorm_identity(la, stream) == hipSuccess ? SAF_OK : SAF_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,540 @@
+// Backward of the SAF hybrid attention layer, bf16, gfx950
+// ("When Can Attention Heads Be Statically Defined?", Section 3.3 and
+// Appendix D.2: key-block programs accumulate value gradients for every head
+// and key gradients for ordinary heads; a separate query-block pass computes
+// query gradients of ordinary heads; frozen heads get dV = W^T dO only).
+//
+// Ordinary heads follow the chain rule of causal softmax attention
+// (Appendix A.1, Equations 5-7) with P recomputed from the saved row
+// log-sum-exp:  P = exp(s*QK^T - L), dP = dO V^T,
+// dS = P o (dP - delta), delta_i = sum_d dO[i][d] * O[i][d],
+// dV = P^T dO, dK = s dS^T Q, dQ = s dS K.
+//
+// Kernels:
+//   bwd_pre : delta for ordinary heads; +0.0 into frozen heads' dQ, dK.
+//   bwd_kv  : one program per (b, h, 128-key block) for ordinary heads and
+//             per (h, 128-key block, batch group) for frozen heads; queries
+//             in tiles of 64.  Accumulators are dV^T and dK^T so that each
+//             lane owns one key and the C registers of S feed the products.
+//   bwd_q   : one program per (b, h, 128-query block) of ordinary heads;
+//             keys in tiles of 64; accumulator dQ^T.
+#include "saf_internal.h"
+#include "saf_tile.h"
+
+namespace saf {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kKvBN = kBwdKvBN;  // keys per key-block program
+constexpr int kKvBM = 64;        // queries per tile in the key-block pass
+constexpr int kQBM = kBwdQBM;    // queries per query-block program
+constexpr int kQBN = 64;         // keys per tile in the query-block pass
+
+template <int D>
+struct BwdCfg {
+  static constexpr int PITCH = D + 8;
+  static constexpr int NDB = D / 32;
+  static constexpr int NKS = D / 16;
+  static constexpr int G = (D <= 64) ? 4 : 2;
+  static constexpr int TILE = 64 * PITCH;
+  static constexpr int BAND = kKvBM + kKvBN;  // r band of a (query tile, key block)
+  // key-block pass, ordinary: Q and dO tiles (double-buffered) + lse2 and delta
+  static constexpr size_t kv_ord_lds = size_t(2) * 2 * TILE * 2 + size_t(2) * 2 * kKvBM * 4;
+  // key-block pass, frozen: G dO tiles (double-buffered) + z2 and the r band
+  static constexpr size_t kv_frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * (kKvBM + BAND) * 4;
+  static constexpr size_t kv_lds = kv_ord_lds > kv_frz_lds ? kv_ord_lds : kv_frz_lds;
+  static constexpr size_t q_lds = size_t(2) * 2 * TILE * 2;
+};
+
+template <int D>
+__device__ __forceinline__ void store_rows_t(const TensorRef& o, int b, int h, int row, int T,
+                                             const f32x16* acc, float mul) {
+  if (row >= T) return;
+  const int hl = lane_id() >> 5;
+  __bf16* p = (__bf16*)o.ptr + (int64_t)b * o.sb + (int64_t)h * o.sh + (int64_t)row * o.st;
+#pragma unroll
+  for (int db = 0; db < BwdCfg<D>::NDB; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * hl;
+      bf16x4 v;
+      v[0] = (__bf16)(acc[db][4 * q4 + 0] * mul);
+      v[1] = (__bf16)(acc[db][4 * q4 + 1] * mul);
+      v[2] = (__bf16)(acc[db][4 * q4 + 2] * mul);
+      v[3] = (__bf16)(acc[db][4 * q4 + 3] * mul);
+      *reinterpret_cast<bf16x4*>(p + d) = v;
+    }
+}
+
+__device__ __forceinline__ float bf16lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+// ---------------------------------------------------------------------------
+// delta = rowsum(dO * O) (ordinary heads); zero dQ, dK (frozen heads).
+// Grid: (ceil(T/256), B*H); one thread per row.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
+  const int bh = blockIdx.y;
+  const int b = bh / A.H, h = bh - b * A.H;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= A.T) return;
+  if (A.is_frozen[h]) {
+    __bf16* dq = (__bf16*)A.dq.ptr + (int64_t)b * A.dq.sb + (int64_t)h * A.dq.sh + (int64_t)i * A.dq.st;
+    __bf16* dk = (__bf16*)A.dk.ptr + (int64_t)b * A.dk.sb + (int64_t)h * A.dk.sh + (int64_t)i * A.dk.st;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      sstore16(dq + 8 * c, u32x4{0u, 0u, 0u, 0u});
+      sstore16(dk + 8 * c, u32x4{0u, 0u, 0u, 0u});
+    }
+    return;
+  }
+  const __bf16* o = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
+  const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh + (int64_t)i * A.dout.st;
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4 x = gload16(o + 8 * c), y = gload16(g + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf16lo(x[e]), bf16lo(y[e]), acc);
+      acc = fmaf(bf16hi(x[e]), bf16hi(y[e]), acc);
+    }
+  }
+  A.delta[((int64_t)b * A.H + h) * A.T + i] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Key-block pass, ordinary head (b, h, kb).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem) {
+  using C = BwdCfg<D>;
+  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int T = A.T;
+  const int k0 = kb * kKvBN;
+  const int j = k0 + 32 * w + (l & 31);  // this lane's key
+  const int wk_lo = k0 + 32 * w;
+
+  const int64_t qoff = (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
+  const int64_t ooff = (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
+  const __bf16* qg = (const __bf16*)A.q.ptr + qoff;
+  const __bf16* dog = (const __bf16*)A.dout.ptr + ooff;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
+  const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+  const float* lse = A.lse + ((int64_t)b * A.H + h) * T;
+  const float* dl = A.delta + ((int64_t)b * A.H + h) * T;
+
+  // K and V rows of this lane's key as B operands (col = key, k = d).
+  bf16x8 kf[C::NKS], vf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    if (j < T) {
+      kf[ks] = __builtin_bit_cast(bf16x8, gload16(kg + (int64_t)j * A.k.st + 16 * ks + 8 * hl));
+      vf[ks] = __builtin_bit_cast(bf16x8, gload16(vg + (int64_t)j * A.v.st + 16 * ks + 8 * hl));
+    } else {
+      kf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      vf[ks] = kf[ks];
+    }
+  }
+
+  __bf16* Qs[2] = {smem, smem + C::TILE};
+  __bf16* Os[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
+  float* fb = (float*)(smem + 4 * C::TILE);
+  float* Ls[2] = {fb, fb + kKvBM};
+  float* Ds[2] = {fb + 2 * kKvBM, fb + 3 * kKvBM};
+
+  const int qt0 = k0 / kKvBM;
+  const int nqt = (T + kKvBM - 1) / kKvBM;
+
+  TileStage<D, kKvBM, kThreads> qst, ost;
+  auto stage_vec = [&](int i0, float* ls, float* ds) {
+    for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
+      const int i = i0 + x;
+      ls[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();  // padding rows: P = 0
+      ds[x] = (i < T) ? dl[i] : 0.f;
+    }
+  };
+  if (qt0 < nqt) {
+    qst.load(qg, A.q.st, qt0 * kKvBM, T);
+    ost.load(dog, A.dout.st, qt0 * kKvBM, T);
+    qst.store(Qs[0], C::PITCH);
+    ost.store(Os[0], C::PITCH);
+    stage_vec(qt0 * kKvBM, Ls[0], Ds[0]);
+  }
+  __syncthreads();
+
+  f32x16 dva[C::NDB], dka[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    dva[db] = f32x16{};
+    dka[db] = f32x16{};
+  }
+  const float sl2 = A.scale_log2;
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int i0 = qt * kKvBM;
+    const int bi = (qt - qt0) & 1;
+    const bool more = (qt + 1) < nqt;
+    if (more) {
+      qst.load(qg, A.q.st, i0 + kKvBM, T);
+      ost.load(dog, A.dout.st, i0 + kKvBM, T);
+    }
+    const __bf16* Q = Qs[bi];
+    const __bf16* O = Os[bi];
+    const float* ls = Ls[bi];
+    const float* ds = Ds[bi];
+    if (i0 + kKvBM - 1 >= wk_lo) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        s[c] = f32x16{};
+        dp[c] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          s[c] = mfma32(lds_frag_nat(Q, C::PITCH, 32 * c, 16 * ks), kf[ks], s[c]);
+          dp[c] = mfma32(lds_frag_nat(O, C::PITCH, 32 * c, 16 * ks), vf[ks], dp[c]);
+        }
+      }
+      const bool diag = i0 < wk_lo + 31;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int ib = 32 * c + 8 * q4 + 4 * hl;  // first of 4 consecutive tile rows
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + ib);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + ib);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q4 + e;
+            float p = fast_exp2(fmaf(s[c][r], sl2, -l4[e]));
+            if (diag && (i0 + ib + e) < j) p = 0.f;
+            s[c][r] = p;
+            dp[c][r] = p * (dp[c][r] - d4[e]);
+          }
+        }
+      // dV^T += dO^T P ; dK^T += Q^T dS
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 pf = pack_acc8(s[st >> 1], 8 * (st & 1));
+        const bf16x8 sf = pack_acc8(dp[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dva[db] = mfma32(lds_frag_tr(O, C::PITCH, 16 * st, 32 * db), pf, dva[db]);
+          dka[db] = mfma32(lds_frag_tr(Q, C::PITCH, 16 * st, 32 * db), sf, dka[db]);
+        }
+      }
+    }
+    if (more) {
+      qst.store(Qs[bi ^ 1], C::PITCH);
+      ost.store(Os[bi ^ 1], C::PITCH);
+      stage_vec(i0 + kKvBM, Ls[bi ^ 1], Ds[bi ^ 1]);
+    }
+    __syncthreads();
+  }
+  store_rows_t<D>(A.dv, b, h, j, T, dva, 1.f);
+  store_rows_t<D>(A.dk, b, h, j, T, dka, A.scale);
+}
+
+// ---------------------------------------------------------------------------
+// Key-block pass, frozen head (h, kb, batch group): dV = W^T dO.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem) {
+  using C = BwdCfg<D>;
+  constexpr int G = C::G;
+  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int T = A.T;
+  const int k0 = kb * kKvBN;
+  const int j = k0 + 32 * w + (l & 31);
+  const int wk_lo = k0 + 32 * w;
+  const int b0 = grp * G;
+  const int nb = min(G, A.B - b0);
+
+  const float* arow = A.a + (int64_t)h * A.prior_len;
+  const float* rrow = A.r + (int64_t)h * A.prior_len;
+  const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
+  const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, same for every b
+
+  __bf16* Os[2] = {smem, smem + G * C::TILE};
+  float* fb = (float*)(smem + 2 * G * C::TILE);
+  float* Zs[2] = {fb, fb + kKvBM + C::BAND};
+  float* Rs[2] = {fb + kKvBM, fb + 2 * kKvBM + C::BAND};
+
+  const int qt0 = k0 / kKvBM;
+  const int nqt = (T + kKvBM - 1) / kKvBM;
+
+  TileStage<D, kKvBM, kThreads> ost[G];
+  auto load_do = [&](int i0) {
+#pragma unroll
+    for (int gb = 0; gb < G; ++gb) {
+      const int b = b0 + (gb < nb ? gb : 0);
+      const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
+      ost[gb].load(g, A.dout.st, i0, T);
+    }
+  };
+  auto store_do = [&](__bf16* dst) {
+#pragma unroll
+    for (int gb = 0; gb < G; ++gb) ost[gb].store(dst + gb * C::TILE, C::PITCH);
+  };
+  // z2 = log N (log2 units) of the tile rows; r band over offsets
+  // [i0 - k0 - (BN-1), i0 + BM - 1 - k0].
+  auto stage_pattern = [&](int i0, float* zs, float* rs) {
+    for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
+      const int i = i0 + x;
+      zs[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();
+    }
+    const int dmin = i0 - k0 - (kKvBN - 1);
+    for (int x = threadIdx.x; x < C::BAND; x += kThreads) {
+      const int d = dmin + x;
+      rs[x] = (d >= 0 && d < T) ? rrow[d] * kLog2e : kNegInf;
+    }
+  };
+
+  if (qt0 < nqt) {
+    load_do(qt0 * kKvBM);
+    store_do(Os[0]);
+    stage_pattern(qt0 * kKvBM, Zs[0], Rs[0]);
+  }
+  __syncthreads();
+
+  f32x16 dva[G][C::NDB];
+#pragma unroll
+  for (int gb = 0; gb < G; ++gb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) dva[gb][db] = f32x16{};
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    const int i0 = qt * kKvBM;
+    const int bi = (qt - qt0) & 1;
+    const bool more = (qt + 1) < nqt;
+    if (more) load_do(i0 + kKvBM);
+    const __bf16* O = Os[bi];
+    const float* zs = Zs[bi];
+    const float* rs = Rs[bi];
+    if (i0 + kKvBM - 1 >= wk_lo) {
+      // band index of (i, j): (i - i0) - (j - k0) + BN - 1
+      const int xj = (kKvBN - 1) - (j - k0);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int ii = 16 * st + 8 * (e >> 2) + 4 * hl + (e & 3);  // tile row
+          wv[e] = fast_exp2(a2 + rs[ii + xj] - zs[ii]);
+        }
+        const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+#pragma unroll
+        for (int gb = 0; gb < G; ++gb)
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            dva[gb][db] = mfma32(lds_frag_tr(O + gb * C::TILE, C::PITCH, 16 * st, 32 * db), wf,
+                                 dva[gb][db]);
+      }
+    }
+    if (more) {
+      store_do(Os[bi ^ 1]);
+      stage_pattern(i0 + kKvBM, Zs[bi ^ 1], Rs[bi ^ 1]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int gb = 0; gb < G; ++gb)
+    if (gb < nb) store_rows_t<D>(A.dv, b0 + gb, h, j, T, dva[gb], 1.f);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs A) {
+  extern __shared__ __align__(16) char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  const int per_k = A.B * A.n_ord + A.n_frz * A.n_groups;
+  const int kb = blockIdx.x / per_k;  // key block 0 has the most queries: first
+  const int rem = blockIdx.x - kb * per_k;
+  if (rem < A.B * A.n_ord) {
+    const int b = rem / A.n_ord;
+    kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], kb, smem);
+  } else {
+    const int f = rem - A.B * A.n_ord;
+    kv_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, kb, smem);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Query-block pass, ordinary head (b, h, qb): dQ = s dS K.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
+  using C = BwdCfg<D>;
+  extern __shared__ __align__(16) char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  const int per_q = A.B * A.n_ord;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
+  const int qb = A.nqb - 1 - qrank;
+  const int b = rem / A.n_ord;
+  const int h = A.ord_heads[rem - b * A.n_ord];
+
+  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int T = A.T;
+  const int q0 = qb * kQBM;
+  const int i = q0 + 32 * w + (l & 31);
+  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+
+  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
+  const __bf16* dog = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
+  const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+
+  bf16x8 qf[C::NKS], of[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    if (i < T) {
+      qf[ks] = __builtin_bit_cast(bf16x8, gload16(qg + (int64_t)i * A.q.st + 16 * ks + 8 * hl));
+      of[ks] = __builtin_bit_cast(bf16x8, gload16(dog + (int64_t)i * A.dout.st + 16 * ks + 8 * hl));
+    } else {
+      qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      of[ks] = qf[ks];
+    }
+  }
+  const int64_t rowv = ((int64_t)b * A.H + h) * T + i;
+  const float l2 = (i < T) ? A.lse[rowv] * kLog2e : __builtin_inff();
+  const float dl = (i < T) ? A.delta[rowv] : 0.f;
+
+  __bf16* Ks[2] = {smem, smem + C::TILE};
+  __bf16* Vs[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
+  const int last_key = min(q0 + kQBM, T) - 1;
+  const int ntiles = last_key / kQBN + 1;
+
+  TileStage<D, kQBN, kThreads> kst, vst;
+  kst.load(kg, A.k.st, 0, T);
+  vst.load(vg, A.v.st, 0, T);
+  kst.store(Ks[0], C::PITCH);
+  vst.store(Vs[0], C::PITCH);
+  __syncthreads();
+
+  f32x16 dqa[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) dqa[db] = f32x16{};
+  const float sl2 = A.scale_log2;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kQBN;
+    const bool more = (t + 1) < ntiles;
+    if (more) {
+      kst.load(kg, A.k.st, j0 + kQBN, T);
+      vst.load(vg, A.v.st, j0 + kQBN, T);
+    }
+    const __bf16* K = Ks[t & 1];
+    const __bf16* V = Vs[t & 1];
+    if (j0 <= wq_hi) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        s[c] = f32x16{};
+        dp[c] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          s[c] = mfma32(lds_frag_nat(K, C::PITCH, 32 * c, 16 * ks), qf[ks], s[c]);
+          dp[c] = mfma32(lds_frag_nat(V, C::PITCH, 32 * c, 16 * ks), of[ks], dp[c]);
+        }
+      }
+      const bool diag = j0 + kQBN - 1 > wq_lo;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = fast_exp2(fmaf(s[c][r], sl2, -l2));
+          if (diag) {
+            const int jj = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (jj > i) p = 0.f;
+          }
+          dp[c][r] = p * (dp[c][r] - dl);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 sf = pack_acc8(dp[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          dqa[db] = mfma32(lds_frag_tr(K, C::PITCH, 16 * st, 32 * db), sf, dqa[db]);
+      }
+    }
+    if (more) {
+      kst.store(Ks[(t + 1) & 1], C::PITCH);
+      vst.store(Vs[(t + 1) & 1], C::PITCH);
+    }
+    __syncthreads();
+  }
+  store_rows_t<D>(A.dq, b, h, i, T, dqa, A.scale);
+}
+
+template <int D>
+hipError_t launch_pre_d(const BwdArgs& args, hipStream_t stream) {
+  dim3 grid((args.T + 255) / 256, args.B * args.H);
+  hipLaunchKernelGGL(bwd_pre_kernel<D>, grid, dim3(256), 0, stream, args);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  args.frz_group = C::G;
+  args.n_groups = (args.B + C::G - 1) / C::G;
+  args.nkb = (args.T + kKvBN - 1) / kKvBN;
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
+  if (grid <= 0) return hipSuccess;
+  static_assert(C::kv_lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(bwd_kv_kernel<D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kv_lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_lds, stream,
+                     args);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
+  using C = BwdCfg<D>;
+  args.nqb = (args.T + kQBM - 1) / kQBM;
+  const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
+  if (grid <= 0) return hipSuccess;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(bwd_q_kernel<D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::q_lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(bwd_q_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::q_lds, stream,
+                     args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_pre_d<64>(args, stream);
+    case 96: return launch_pre_d<96>(args, stream);
+    case 128: return launch_pre_d<128>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_kv_d<64>(args, stream);
+    case 96: return launch_kv_d<96>(args, stream);
+    case 128: return launch_kv_d<128>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_q_d<64>(args, stream);
+    case 96: return launch_q_d<96>(args, stream);
+    case 128: return launch_q_d<128>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace saf

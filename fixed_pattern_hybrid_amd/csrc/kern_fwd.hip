@@ -1,0 +1,337 @@
+// Mixed-head forward of the SAF hybrid attention layer, bf16, gfx950.
+//
+// One launch covers every head ("When Can Attention Heads Be Statically
+// Defined?", Section 3.3 "Fused computation" and Appendix D.2): each program
+// reads the head-state flag of its head and runs either
+//   * an ordinary program (b, h, query block): online-softmax tiling of
+//     causal attention (Appendix A.1, Equations 5-7), or
+//   * a frozen program (h, query block, group of batch elements): each causal
+//     tile of the compact pattern (Section 3.2, Equation 3) is rebuilt in
+//     registers once from a, r and the precomputed row normalisers, then
+//     multiplied with the value tiles of every batch element in the group.
+//     The weights do not depend on the batch index, so rebuilding them once
+//     per group divides the exp work by the group size.
+// Outputs are written in the original head order.
+//
+// Work layout: 4 waves, 32 queries per wave, key tiles of 64.  Products are
+// computed transposed (S^T = K Q^T, O^T = V^T P^T) so that every lane owns
+// one query: row max, row sum and rescaling stay in the lane, and the C
+// registers of S^T convert directly into the B operand of the second product.
+#include "saf_internal.h"
+#include "saf_tile.h"
+
+namespace saf {
+namespace {
+
+constexpr int kBM = kFwdBM;  // queries per program
+constexpr int kBN = 64;      // keys per tile
+constexpr int kThreads = 256;
+
+template <int D>
+struct FwdCfg {
+  static constexpr int PITCH = D + 8;  // LDS row pitch (elements)
+  static constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
+  static constexpr int NKS = D / 16;   // 16-deep k steps over the head dimension
+  static constexpr int G = (D <= 64) ? 4 : 2;  // batch elements per frozen program
+  static constexpr int TILE = kBN * PITCH;     // elements of one staged tile
+  static constexpr int BAND = kBM + kBN;       // r band length (BM + BN - 1, padded)
+  static constexpr size_t ord_lds = size_t(2) * 2 * TILE * 2;
+  static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * (kBN + BAND) * 4;
+  static constexpr size_t lds = ord_lds > frz_lds ? ord_lds : frz_lds;
+};
+
+template <int D>
+__device__ __forceinline__ void store_out_rows(const TensorRef& o, int b, int h, int i, int T,
+                                               const f32x16* acc, float mul) {
+  if (i >= T) return;
+  const int hl = lane_id() >> 5;
+  __bf16* row = (__bf16*)o.ptr + (int64_t)b * o.sb + (int64_t)h * o.sh + (int64_t)i * o.st;
+#pragma unroll
+  for (int db = 0; db < FwdCfg<D>::NDB; ++db) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * db + 8 * q4 + 4 * hl;
+      bf16x4 v;
+      v[0] = (__bf16)(acc[db][4 * q4 + 0] * mul);
+      v[1] = (__bf16)(acc[db][4 * q4 + 1] * mul);
+      v[2] = (__bf16)(acc[db][4 * q4 + 2] * mul);
+      v[3] = (__bf16)(acc[db][4 * q4 + 3] * mul);
+      *reinterpret_cast<bf16x4*>(row + d) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Ordinary head: causal softmax attention with an online row maximum.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* smem) {
+  using C = FwdCfg<D>;
+  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int T = A.T;
+  const int q0 = qb * kBM;
+  const int i = q0 + 32 * w + (l & 31);  // this lane's query
+  const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
+
+  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
+  const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[i][16ks + 8*hl + 0..7].
+  bf16x8 qf[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    if (i < T) {
+      qf[ks] = __builtin_bit_cast(bf16x8, gload16(qg + (int64_t)i * A.q.st + 16 * ks + 8 * hl));
+    } else {
+      qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  __bf16* Ks[2] = {smem, smem + C::TILE};
+  __bf16* Vs[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
+
+  const int last_key = min(q0 + kBM, T) - 1;
+  const int ntiles = last_key / kBN + 1;
+
+  TileStage<D, kBN, kThreads> kst, vst;
+  kst.load(kg, A.k.st, 0, T);
+  vst.load(vg, A.v.st, 0, T);
+  kst.store(Ks[0], C::PITCH);
+  vst.store(Vs[0], C::PITCH);
+  __syncthreads();
+
+  f32x16 oacc[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) oacc[db] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  const float sl2 = A.scale_log2;
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kBN;
+    const bool more = (t + 1) < ntiles;
+    if (more) {
+      kst.load(kg, A.k.st, j0 + kBN, T);
+      vst.load(vg, A.v.st, j0 + kBN, T);
+    }
+    const __bf16* K = Ks[t & 1];
+    const __bf16* V = Vs[t & 1];
+    if (j0 <= wq_hi) {
+      f32x16 s[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        s[c] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks)
+          s[c] = mfma32(lds_frag_nat(K, C::PITCH, 32 * c, 16 * ks), qf[ks], s[c]);
+      }
+      // causal mask where the tile reaches past this wave's first query
+      if (j0 + kBN - 1 > wq_lo) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if (j > i) s[c][r] = kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float alpha = fast_exp2(m_run - m_new);
+      float psum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[c][r], sl2, -m_new));
+          s[c][r] = p;
+          psum += p;
+        }
+      l_run = fmaf(l_run, alpha, psum);
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const bf16x8 pf = pack_acc8(s[st >> 1], 8 * (st & 1));
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          oacc[db] = mfma32(lds_frag_tr(V, C::PITCH, 16 * st, 32 * db), pf, oacc[db]);
+      }
+    }
+    if (more) {
+      kst.store(Ks[(t + 1) & 1], C::PITCH);
+      vst.store(Vs[(t + 1) & 1], C::PITCH);
+    }
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + xor32(l_run);
+  store_out_rows<D>(A.o, b, h, i, T, oacc, 1.f / l_tot);
+  if (hl == 0 && i < T) A.lse[((int64_t)b * A.H + h) * T + i] = (m_run + fast_log2(l_tot)) * kLn2;
+}
+
+// ---------------------------------------------------------------------------
+// Frozen head: W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* smem) {
+  using C = FwdCfg<D>;
+  constexpr int G = C::G;
+  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int T = A.T;
+  const int q0 = qb * kBM;
+  const int i = q0 + 32 * w + (l & 31);
+  const int wq_hi = q0 + 32 * w + 31;
+  const int b0 = grp * G;
+  const int nb = min(G, A.B - b0);
+
+  __bf16* Vs[2] = {smem, smem + G * C::TILE};
+  float* fbase = (float*)(smem + 2 * G * C::TILE);
+  float* As[2] = {fbase, fbase + kBN + C::BAND};
+  float* Rs[2] = {fbase + kBN, fbase + 2 * kBN + C::BAND};
+
+  const float* arow = A.a + (int64_t)h * A.prior_len;
+  const float* rrow = A.r + (int64_t)h * A.prior_len;
+  const float z2 = (i < T) ? A.lse[((int64_t)b0 * A.H + h) * T + i] * kLog2e : 0.f;
+
+  const int last_key = min(q0 + kBM, T) - 1;
+  const int ntiles = last_key / kBN + 1;
+
+  // a (log2 units) for tile keys and the reversed-free r band of the tile.
+  auto stage_pattern = [&](int j0, float* as, float* rs) {
+    for (int x = threadIdx.x; x < kBN; x += kThreads) {
+      const int j = j0 + x;
+      as[x] = (j < T) ? arow[j] * kLog2e : kNegInf;
+    }
+    const int dmin = q0 - j0 - (kBN - 1);
+    for (int x = threadIdx.x; x < C::BAND; x += kThreads) {
+      const int dl = dmin + x;
+      rs[x] = (dl >= 0 && dl < T) ? rrow[dl] * kLog2e : kNegInf;
+    }
+  };
+
+  TileStage<D, kBN, kThreads> vst[G];
+  auto load_v = [&](int j0) {
+#pragma unroll
+    for (int gb = 0; gb < G; ++gb) {
+      const int b = b0 + (gb < nb ? gb : 0);
+      const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+      vst[gb].load(vg, A.v.st, j0, T);
+    }
+  };
+  auto store_v = [&](__bf16* dst) {
+#pragma unroll
+    for (int gb = 0; gb < G; ++gb) vst[gb].store(dst + gb * C::TILE, C::PITCH);
+  };
+
+  load_v(0);
+  stage_pattern(0, As[0], Rs[0]);
+  store_v(Vs[0]);
+  __syncthreads();
+
+  f32x16 oacc[G][C::NDB];
+#pragma unroll
+  for (int gb = 0; gb < G; ++gb)
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) oacc[gb][db] = f32x16{};
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * kBN;
+    const bool more = (t + 1) < ntiles;
+    if (more) load_v(j0 + kBN);
+    const __bf16* V = Vs[t & 1];
+    const float* as = As[t & 1];
+    const float* rs = Rs[t & 1];
+    if (j0 <= wq_hi) {
+      // band index of (i, j): (i - q0) - (j - j0) + BN - 1
+      const int xi = (i - q0) + kBN - 1;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int jj = 16 * st + 8 * (e >> 2) + 4 * hl + (e & 3);
+          wv[e] = fast_exp2(as[jj] + rs[xi - jj] - z2);
+        }
+        const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
+#pragma unroll
+        for (int gb = 0; gb < G; ++gb)
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+            oacc[gb][db] = mfma32(lds_frag_tr(V + gb * C::TILE, C::PITCH, 16 * st, 32 * db), wf,
+                                  oacc[gb][db]);
+      }
+    }
+    if (more) {
+      store_v(Vs[(t + 1) & 1]);
+      stage_pattern(j0 + kBN, As[(t + 1) & 1], Rs[(t + 1) & 1]);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int gb = 0; gb < G; ++gb)
+    if (gb < nb) store_out_rows<D>(A.o, b0 + gb, h, i, T, oacc[gb], 1.f);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs A) {
+  extern __shared__ __align__(16) char smem_raw[];
+  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  const int per_q = A.B * A.n_ord + A.n_frz * A.n_groups;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
+  const int qb = A.nqb - 1 - qrank;  // longest query blocks first
+  if (rem < A.B * A.n_ord) {
+    const int b = rem / A.n_ord;
+    const int h = A.ord_heads[rem - b * A.n_ord];
+    fwd_ordinary<D>(A, b, h, qb, smem);
+  } else {
+    const int f = rem - A.B * A.n_ord;
+    const int h = A.frz_heads[f / A.n_groups];
+    fwd_frozen<D>(A, h, f % A.n_groups, qb, smem);
+  }
+}
+
+template <int D>
+hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  args.frz_group = C::G;
+  args.n_groups = (args.B + C::G - 1) / C::G;
+  args.nqb = (args.T + kBM - 1) / kBM;
+  const int per_q = args.B * args.n_ord + args.n_frz * args.n_groups;
+  const int64_t grid = (int64_t)per_q * args.nqb;
+  if (grid <= 0) return hipSuccess;
+  static_assert(C::lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(fwd_bf16_kernel<D>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::lds, stream,
+                     args);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_fwd_d<64>(args, stream);
+    case 96: return launch_fwd_d<96>(args, stream);
+    case 128: return launch_fwd_d<128>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace saf

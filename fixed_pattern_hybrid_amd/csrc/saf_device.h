@@ -1,0 +1,120 @@
+// Device helpers for gfx950 (CDNA4, wave64): bf16 MFMA fragments, LDS
+// fragment reads and small conversions.
+//
+// MFMA v_mfma_f32_32x32x16_bf16, C[32x32] += A[32x16] * B[16x32]:
+//   A: lane l holds row (l % 32), k = 8*(l/32) + e for e = 0..7
+//   B: lane l holds col (l % 32), k = 8*(l/32) + e
+//   C: lane l, register r holds col (l % 32), row 8*(r/4) + 4*(l/32) + r%4
+// (verified on the device).  The contraction index k may be relabelled freely
+// as long as A and B use the same labelling; the kernels use that to feed
+// softmax / pattern weights straight from C registers into the next product.
+//
+// ds_read_b64_tr_b16 (LDS transpose read), per group of 16 lanes: if source
+// lane 4e + c of the group addresses 4 consecutive 16-bit values starting at
+// X[R + e][C + 4c], then output lane t of the group receives
+// X[R + 0..3][C + t].  Two such reads give an MFMA operand whose k index runs
+// along the rows of a row-major LDS tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saf {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Round 8 fp32 values to bf16 (nearest-even) and pack them as an operand.
+__device__ __forceinline__ bf16x8 pack_bf16x8(float x0, float x1, float x2, float x3, float x4,
+                                              float x5, float x6, float x7) {
+  bf16x8 v;
+  v[0] = (__bf16)x0; v[1] = (__bf16)x1; v[2] = (__bf16)x2; v[3] = (__bf16)x3;
+  v[4] = (__bf16)x4; v[5] = (__bf16)x5; v[6] = (__bf16)x6; v[7] = (__bf16)x7;
+  return v;
+}
+
+// Operand registers r0..r0+7 of an accumulator as a bf16 fragment.
+__device__ __forceinline__ bf16x8 pack_acc8(const f32x16& c, int r0) {
+  return pack_bf16x8(c[r0], c[r0 + 1], c[r0 + 2], c[r0 + 3], c[r0 + 4], c[r0 + 5], c[r0 + 6],
+                     c[r0 + 7]);
+}
+
+// 16-byte LDS read: 8 consecutive bf16 at element offset `off` of `base`.
+__device__ __forceinline__ bf16x8 lds_read8(const __bf16* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+
+// Transposed 4-element read (see header comment); `off` is the element
+// offset this lane addresses.
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* base, int off) {
+  const lds_char* p = (const lds_char*)(base) + 2 * off;
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(bf16x4, t);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
+  bf16x8 v;
+  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+  return v;
+}
+
+// MFMA operand whose k index runs along rows of a row-major LDS tile X with
+// row pitch `pitch` (elements).  Lane l receives
+//   X[row0 + 4*(l/32) + e][col0 + l%32]       for e = 0..3 (slots 0..3)
+//   X[row0 + 8 + 4*(l/32) + e][col0 + l%32]   for e = 0..3 (slots 4..7)
+// i.e. slot e of half h maps to row row0 + 8*(e/4) + 4*h + e%4 -- exactly the
+// row labelling of the C registers 8*(s%2)..8*(s%2)+7 of a 32x32 accumulator
+// block, so a C block converted with pack_acc8 pairs with this operand.
+__device__ __forceinline__ bf16x8 lds_frag_tr(const __bf16* X, int pitch, int row0, int col0) {
+  const int l = lane_id();
+  const int g = l >> 4;        // 16-lane group
+  const int s16 = l & 15;
+  const int e = s16 >> 2, c = s16 & 3;
+  const int row = row0 + 4 * (g >> 1) + e;
+  const int col = col0 + 16 * (g & 1) + 4 * c;
+  bf16x4 lo = lds_read_tr4(X, row * pitch + col);
+  bf16x4 hi = lds_read_tr4(X, (row + 8) * pitch + col);
+  return cat8(lo, hi);
+}
+
+// MFMA operand whose k index runs along columns of a row-major LDS tile:
+// lane l receives X[row0 + l%32][col0 + 8*(l/32) + e], e = 0..7.
+__device__ __forceinline__ bf16x8 lds_frag_nat(const __bf16* X, int pitch, int row0, int col0) {
+  const int l = lane_id();
+  return lds_read8(X, (row0 + (l & 31)) * pitch + col0 + 8 * (l >> 5));
+}
+
+// Exchange with the lane 32 positions away (the other half of a C column).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Vector loads/stores of 16 bytes from global memory.
+__device__ __forceinline__ u32x4 gload16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void sstore16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+}  // namespace saf

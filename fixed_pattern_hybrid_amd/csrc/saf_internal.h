@@ -1,0 +1,88 @@
+// Internal declarations shared by the C-ABI layer and the kernel sources.
+// Kernel argument blocks are plain structs passed by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace saf {
+
+constexpr int kMaxHeads = 256;
+
+// One strided [B][H][T][D] tensor: base pointer and element strides of
+// (b, h, t); the d stride is 1.
+struct TensorRef {
+  void* ptr;
+  int64_t sb, sh, st;
+};
+
+// Forward arguments (both dtypes).
+struct FwdArgs {
+  TensorRef q, k, v, o;
+  const float* a;    // [H][prior_len]
+  const float* r;    // [H][prior_len]
+  float* lse;        // [B][H][T]; frozen heads' rows already hold log N
+  int B, H, T, prior_len;
+  float scale_log2;  // softmax_scale * log2(e)
+  int n_ord, n_frz;  // number of ordinary / frozen heads
+  int frz_group;     // batch elements per frozen program
+  int n_groups;      // ceil(B / frz_group)
+  int nqb;           // number of query blocks
+  uint8_t ord_heads[kMaxHeads];
+  uint8_t frz_heads[kMaxHeads];
+};
+
+// Backward arguments (both dtypes).
+struct BwdArgs {
+  TensorRef q, k, v, o, dout, dq, dk, dv;
+  const float* a;
+  const float* r;
+  const float* lse;  // [B][H][T]
+  float* delta;      // workspace [B][H][T]: rowsum(dO * O) of ordinary heads
+  int B, H, T, prior_len;
+  float scale;       // softmax_scale
+  float scale_log2;  // softmax_scale * log2(e)
+  int n_ord, n_frz;
+  int frz_group, n_groups;
+  int nqb, nkb;      // query / key blocks of the respective passes
+  uint8_t ord_heads[kMaxHeads];
+  uint8_t frz_heads[kMaxHeads];
+  uint8_t is_frozen[kMaxHeads];
+};
+
+// Normaliser arguments: for each listed head h, logZ over rows [0, T) is
+// written to out[(b * H + h) * T + i] for every b in [0, B).
+struct LognormArgs {
+  const float* a;
+  const float* r;
+  float* out;
+  int64_t out_b_stride;  // elements between batch copies (0 for one copy)
+  int64_t out_h_stride;  // elements between head rows of out
+  int n_heads;           // entries of heads[]
+  int B;                 // number of batch copies to write
+  int T, prior_len;
+  uint8_t heads[kMaxHeads];
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream);
+hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const float* r, float* w,
+                                hipStream_t stream);
+
+hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream);
+
+hipError_t launch_fwd_f32(const FwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_pre_f32(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_f32(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_q_f32(const BwdArgs& args, int D, hipStream_t stream);
+
+// Tile geometry of the bf16 kernels (used by the host for grid sizes).
+constexpr int kFwdBM = 128;     // queries per forward program
+constexpr int kBwdKvBN = 128;   // keys per key-block program
+constexpr int kBwdQBM = 128;    // queries per query-block program
+constexpr int kFrzGroup = 4;    // batch elements sharing one rebuilt pattern tile
+
+}  // namespace saf

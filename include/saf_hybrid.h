@@ -1,0 +1,169 @@
+/*
+ * saf_hybrid.h -- C ABI of the SAF hybrid attention library for AMD MI355X
+ * (gfx950 / CDNA4).
+ *
+ * The layer is one causal multi-head attention pass with two kinds of head
+ * ("When Can Attention Heads Be Statically Defined?", Section 3.3 "Fused
+ * computation" and Appendix D.2):
+ *
+ *   ordinary head (Appendix A.1, Equations 5-7):
+ *       S = s * Q K^T, A = causal row softmax of S, O = A V,
+ *       s = softmax_scale (default 1/sqrt(D));
+ *   frozen head (Section 3.2, Equation 3):
+ *       W[i][j] = exp(a[j] + r[i-j]) / N(i) for j <= i, 0 for j > i,
+ *       N(i) = sum_{k<=i} exp(a[k] + r[i-k]),  O = W V.
+ *       Q and K of a frozen head are never read; the logits carry no scale.
+ *
+ * Indices are 0-based: a[j] is the pages' alpha(j+1) and r[d] is rho(d).
+ * Backward (Section 3.3 and Appendix D.2): ordinary heads get dQ, dK, dV of
+ * the softmax attention; frozen heads get dV = W^T dO and exact +0.0 in their
+ * dQ and dK slices (a frozen head has no query/key slot).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *    library never allocates device memory; scratch space is passed in as a
+ *    workspace sized by saf_hybrid_attn_workspace_bytes().
+ *  - Q, K, V, O, dO, dQ, dK, dV have logical shape [B][H][T][D].  Their
+ *    element strides for (b, h, t) are given per tensor; the stride of the
+ *    last (d) dimension must be 1.  Base pointers must be 16-byte aligned
+ *    and each (b, h, t) stride a multiple of 16 bytes.
+ *  - a and r are fp32 [H][prior_len] (row stride prior_len, prior_len >= T);
+ *    rows of ordinary heads are never read.  Only entries [0, T) of a row are
+ *    used, which is exact: causal rows never reach further.
+ *  - lse is fp32 [B][H][T] contiguous.  For an ordinary head it holds the
+ *    natural-log log-sum-exp of row i of s*QK^T; for a frozen head it holds
+ *    log N(i) (the same for every b).  The forward writes it, the backward
+ *    reads it.
+ *  - dtype SAF_BF16: Q, K, V, dO and all outputs are bfloat16; products run
+ *    on bf16 MFMA with fp32 accumulation, softmax and pattern weights are
+ *    computed in fp32 and rounded to nearest-even bf16 before the second
+ *    product.  dtype SAF_F32: everything is fp32.
+ *  - Every argument is validated before anything is enqueued; on error
+ *    nothing is launched and outputs are untouched.  The return value is a
+ *    status code (SAF_OK or a negative SAF_E* value).
+ *  - Work is enqueued asynchronously on `stream` (0 = the null stream) and
+ *    the call never synchronises.  A failed launch returns SAF_EHIP; faults
+ *    inside a kernel surface at the caller's next synchronisation.
+ *  - The library has no mutable global state; concurrent calls on different
+ *    streams are safe.  Results are bitwise deterministic (no atomics).
+ */
+#ifndef SAF_HYBRID_H
+#define SAF_HYBRID_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SAF_OK 0
+#define SAF_EINVAL (-1)       /* bad pointer, size, stride or alignment */
+#define SAF_EUNSUPPORTED (-2) /* valid but not implemented: D, dtype, H */
+#define SAF_EWORKSPACE (-3)   /* workspace missing or too small */
+#define SAF_EHIP (-4)         /* a HIP launch or runtime call failed */
+
+/* Element types of Q, K, V, O, dO, dQ, dK, dV. */
+#define SAF_F32 0
+#define SAF_BF16 1
+
+/* Limits. */
+#define SAF_MAX_HEADS 256
+#define SAF_MAX_T (1 << 20)
+
+/*
+ * Shape, layout and head-state description of one call.
+ * Fill every field; set struct_bytes = sizeof(saf_attn_params) (checked, so
+ * that a binding with a different layout is rejected instead of misread).
+ */
+typedef struct saf_attn_params {
+  uint32_t struct_bytes;
+  int32_t B, H, T, D;       /* D in {64, 96, 128} for bf16; {16, 32, 64, 96, 128} for fp32 */
+  int32_t prior_len;        /* stored length of each a/r row, >= T */
+  int32_t dtype;            /* SAF_F32 or SAF_BF16 */
+  float softmax_scale;      /* ordinary heads; <= 0 selects 1/sqrt(D) */
+  /* element strides of dimensions (b, h, t); the d stride is 1 */
+  int64_t q_stride[3], k_stride[3], v_stride[3], o_stride[3];
+  int64_t do_stride[3], dq_stride[3], dk_stride[3], dv_stride[3];
+  /* HOST array [H]: 1 = frozen head, 0 = ordinary head (the per-head state
+   * flag of Section 3.3).  Read during the call only. */
+  const uint8_t* frozen;
+  /* Optional instrumentation: a HOST array of n_stage_events events created
+   * by the caller.  When non-NULL, event 0 is recorded on `stream` before the
+   * first kernel and event k after the k-th kernel of the call (k <= n-1);
+   * kernels beyond n-1 are not bracketed.  Nothing is skipped or changed. */
+  hipEvent_t* stage_events;
+  int32_t n_stage_events;
+  int32_t reserved1;        /* must be 0 */
+} saf_attn_params;
+
+/*
+ * Forward pass of the hybrid layer (Section 3.3 "Fused computation";
+ * Appendix D.2): O in the original head order and lse.
+ *   q, k, v : device [B][H][T][D] (strided as in p); frozen heads' q, k are
+ *             not read and may hold anything (also NaN).
+ *   a, r    : device fp32 [H][prior_len].
+ *   o       : device [B][H][T][D] output.
+ *   lse     : device fp32 [B][H][T] output (see conventions above).
+ *   ws      : workspace of at least saf_hybrid_attn_workspace_bytes(p, 0)
+ *             bytes, 256-byte aligned (may be NULL when that is 0).
+ * Kernels: the frozen heads' row normalisers, then one mixed-head launch.
+ */
+int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k,
+                        const void* v, const float* a, const float* r, void* o,
+                        float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Backward pass of the hybrid layer (Section 3.3; Appendix D.2 key-block and
+ * query-block passes).  Given dO and the forward's o and lse, writes
+ *   dq, dk : ordinary heads' gradients; frozen heads' slices := +0.0;
+ *   dv     : gradients of every head (frozen: W^T dO).
+ * q, k of frozen heads are not read.  o is read for ordinary heads only.
+ * ws: at least saf_hybrid_attn_workspace_bytes(p, 1) bytes, 256-byte aligned.
+ */
+int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k,
+                        const void* v, const void* o, const void* dout,
+                        const float* lse, const float* a, const float* r,
+                        void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Workspace bytes a call with these parameters needs (0 if none);
+ * for_bwd = 0 for the forward, 1 for the backward.  Returns 0 for invalid p. */
+size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd);
+
+/*
+ * Dense compact pattern of one frozen head (Section 3.2, Equation 3), as an
+ * eager reference: w[i][j] = exp(a[j] + r[i-j] - log N(i)) for j <= i and 0
+ * above the diagonal.
+ *   a, r : device fp32, at least prior_len (>= T) entries each.
+ *   w    : device fp32 [T][T] row-major output (T*T*4 bytes).
+ * T must be in [1, 32768].
+ */
+int saf_pattern_dense(int32_t T, int32_t prior_len, const float* a,
+                      const float* r, float* w, hipStream_t stream);
+
+/*
+ * Row normalisers of frozen patterns (Section 3.2, Equation 3), computed
+ * with a max-shifted log-sum-exp:
+ *   logz[h][i] = log sum_{k<=i} exp(a[h][k] + r[h][i-k]),  0 <= i < T,
+ * for n_heads rows of a, r (device fp32 [n_heads][prior_len]) into logz
+ * (device fp32 [n_heads][T]).
+ */
+int saf_pattern_lognorm(int32_t n_heads, int32_t T, int32_t prior_len,
+                        const float* a, const float* r, float* logz,
+                        hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* saf_status_string(int status);
+
+/* Library version as (major << 16) | minor. */
+int32_t saf_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAF_HYBRID_H */

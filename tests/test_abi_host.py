@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+declared in include/saf_hybrid.h, its parameter block matches the binding, and
+invalid arguments are rejected before anything touches the GPU."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "saf_hybrid.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(saf_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def b():
+    from fixed_pattern_hybrid_amd import binding
+
+    return binding
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared_functions()
+    for n in ("saf_hybrid_attn_fwd", "saf_hybrid_attn_bwd", "saf_pattern_dense"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(b):
+    for n in _declared_functions():
+        assert hasattr(b.LIB, n), n
+    assert set(_declared_functions()) == set(b.EXPORTED)
+
+
+def test_param_block_layout_matches_c(tmp_path, b):
+    src = tmp_path / "sz.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "saf_hybrid.h"\n'
+        "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(saf_attn_params),"
+        " offsetof(saf_attn_params, q_stride), offsetof(saf_attn_params, dv_stride),"
+        " offsetof(saf_attn_params, frozen), offsetof(saf_attn_params, n_stage_events));return 0;}\n"
+    )
+    exe = tmp_path / "sz"
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{ROOT}/include",
+                    str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
+    P = b.SafParams
+    want = [ctypes.sizeof(P), P.q_stride.offset, P.dv_stride.offset, P.frozen.offset, P.n_stage_events.offset]
+    assert got == want
+
+
+def test_status_strings(b):
+    for s in (0, -1, -2, -3, -4, 7):
+        assert isinstance(b.status_string(s), str) and b.status_string(s)
+    assert b.version()[0] >= 1
+
+
+def _params(b, **kw):
+    H = kw.get("H", 4)
+    p = b.SafParams()
+    p.struct_bytes = ctypes.sizeof(b.SafParams)
+    p.B, p.H, p.T, p.D = kw.get("B", 1), H, kw.get("T", 16), kw.get("D", 64)
+    p.prior_len = kw.get("prior_len", p.T)
+    p.dtype = kw.get("dtype", b.SAF_BF16)
+    p.softmax_scale = kw.get("scale", 0.0)
+    for n in ("q", "k", "v", "o", "do", "dq", "dk", "dv"):
+        setattr(p, n + "_stride", b._i64x3(p.H * p.T * p.D, p.T * p.D, p.D))
+    arr = (ctypes.c_uint8 * H)(*kw.get("frozen", [0] * H))
+    p.frozen = ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8))
+    return p, arr
+
+
+FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on these paths
+
+
+@pytest.mark.parametrize(
+    "mut,expect",
+    [
+        ({"struct_bytes": 3}, -1),
+        ({"B": 0}, -1),
+        ({"T": 0}, -1),
+        ({"H": 300}, -2),
+        ({"D": 80}, -2),
+        ({"dtype": 5}, -2),
+        ({"prior_len": 8}, -1),
+        ({"reserved1": 1}, -1),
+        ({"softmax_scale": float("nan")}, -1),
+    ],
+)
+def test_fwd_rejects_bad_params(b, mut, expect):
+    p, arr = _params(b)
+    for k, v in mut.items():
+        setattr(p, k, v)
+    st = b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == expect
+
+
+def test_fwd_rejects_bad_pointers_and_strides(b):
+    p, arr = _params(b)
+    call = lambda *x: b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *x, None, 0, None)  # noqa: E731
+    assert call(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == -1  # q null, ordinary heads present
+    assert call(FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == -1  # misaligned
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1  # lse null
+    p.q_stride = b._i64x3(0, 0, 12)  # t stride not a multiple of 16 bytes
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == -1
+    p2, arr2 = _params(b, frozen=[1, 1, 1, 1])  # all frozen: q/k unused, a/r required
+    st = b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p2), None, None, FAKE, None, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == -1
+    p3, arr3 = _params(b, frozen=[0, 2, 0, 0])  # flags must be 0/1
+    st = b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p3), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == -1
+
+
+def test_bwd_workspace_checks(b):
+    p, arr = _params(b, B=2, H=4, T=100)
+    need = b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 1)
+    assert need >= 2 * 4 * 100 * 4 and need % 256 == 0
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0) == 0
+    args = [FAKE] * 11
+    assert b.LIB.saf_hybrid_attn_bwd(ctypes.byref(p), *args, None, need, None) == -3
+    assert b.LIB.saf_hybrid_attn_bwd(ctypes.byref(p), *args, FAKE, need - 1, None) == -3
+    assert b.LIB.saf_hybrid_attn_bwd(ctypes.byref(p), *args, FAKE + 16, need, None) == -3
+    bad, _ = _params(b, D=48)
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(bad), 1) == 0
+
+
+def test_pattern_entry_points_reject(b):
+    assert b.LIB.saf_pattern_dense(0, 4, FAKE, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_dense(8, 4, FAKE, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_dense(40000, 40000, FAKE, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_dense(8, 8, None, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_lognorm(0, 8, 8, FAKE, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_lognorm(2, 8, 7, FAKE, FAKE, FAKE, None) == -1
+    assert b.LIB.saf_pattern_lognorm(2, 8, 8, FAKE, FAKE, FAKE + 1, None) == -1
+
+
+def test_binding_has_no_cpu_fallback():
+    src = open(os.path.join(ROOT, "fixed_pattern_hybrid_amd", "binding.py")).read()
+    assert "oracle" not in src and "import numpy" not in src

@@ -1,0 +1,303 @@
+"""Parity of the HIP path with the float64 oracle (GPU required).
+
+Small shapes compare every element; the workload shapes compare sampled heads
+(and, for the 32K prefill, sampled rows) that the oracle computes one by one,
+plus properties that hold at any size.  Inputs come from the seeded
+generator in ``synth``; expected values come only from ``oracle``.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import CONFIGS, get_config, make_inputs
+from _helpers import (
+    BF16_FWD_MAXABS, BF16_FWD_RELL2, BF16_GRAD_RELL2, F32_MAXABS, F32_RELL2, LSE_FRZ_ABS,
+    LSE_ORD_ABS, host, max_abs, rel_l2, say, upload,
+)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fixed_pattern_hybrid_amd import binding
+
+    return binding
+
+
+def _bars(cfg):
+    if cfg.dtype == "bf16":
+        return dict(o_max=BF16_FWD_MAXABS, o_rel=BF16_FWD_RELL2, g_rel=BF16_GRAD_RELL2, g_max=None)
+    return dict(o_max=F32_MAXABS, o_rel=F32_RELL2, g_rel=F32_RELL2, g_max=None)
+
+
+def _check_head(tag, cfg, got_o, ref_o, got_l, ref_l, frozen_h):
+    bars = _bars(cfg)
+    e_max, e_rel = max_abs(got_o, ref_o), rel_l2(got_o, ref_o)
+    e_l = max_abs(got_l, ref_l)
+    say(f"  {tag}: O max-abs {e_max:.3e} rel-L2 {e_rel:.3e} lse max-abs {e_l:.3e}")
+    assert e_max <= bars["o_max"], (tag, e_max)
+    assert e_rel <= bars["o_rel"], (tag, e_rel)
+    assert e_l <= (LSE_FRZ_ABS if frozen_h else LSE_ORD_ABS), (tag, e_l)
+
+
+def run_full_parity(B, cfg, seed=None, strided=False, poison_frozen_qk=False, scale=None):
+    """Forward and backward on every element of a small case."""
+    say(f"case {cfg.name} B={cfg.B} H={cfg.H} T={cfg.T} D={cfg.D} Tp={cfg.Tp} frozen={cfg.frozen} "
+        f"{cfg.dtype} strided={strided} poison={poison_frozen_qk} seed={seed}")
+    inp = make_inputs(cfg, seed, with_do=True)
+    dev = upload(inp)
+    q, k, v, do = dev["q"], dev["k"], dev["v"], dev["do"]
+    if strided:
+        # [B, T, H, D] storage seen as [B, H, T, D] (non-contiguous Q/K/V views)
+        q = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        assert not q.is_contiguous()
+    fz = [int(x) for x in inp.frozen]
+    if poison_frozen_qk:
+        q = q.clone()
+        k = k.clone()
+        for h in range(cfg.H):
+            if fz[h]:
+                q[:, h] = float("nan")
+                k[:, h] = float("nan")
+    O, L = B.saf_hybrid_attn_fwd(q, k, v, fz, dev["a"], dev["r"], softmax_scale=scale)
+    dq, dk, dv = B.saf_hybrid_attn_bwd(q, k, v, O, do, L, fz, dev["a"], dev["r"], softmax_scale=scale)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.hybrid_fwd(inp.q, inp.k, inp.v, fz, inp.a, inp.r, scale=scale)
+    ref_dq, ref_dk, ref_dv = oracle.hybrid_bwd(inp.q, inp.k, inp.v, inp.do, fz, inp.a, inp.r, scale=scale)
+    got = {n: host(t) for n, t in dict(o=O, l=L, dq=dq, dk=dk, dv=dv).items()}
+    bars = _bars(cfg)
+    e = {
+        "O": (max_abs(got["o"], ref_o), rel_l2(got["o"], ref_o)),
+        "dQ": (max_abs(got["dq"], ref_dq), rel_l2(got["dq"], ref_dq)),
+        "dK": (max_abs(got["dk"], ref_dk), rel_l2(got["dk"], ref_dk)),
+        "dV": (max_abs(got["dv"], ref_dv), rel_l2(got["dv"], ref_dv)),
+    }
+    for n, (m, r) in e.items():
+        say(f"  {n}: max-abs {m:.3e} rel-L2 {r:.3e}")
+    assert e["O"][0] <= bars["o_max"] and e["O"][1] <= bars["o_rel"], e["O"]
+    refs = {"dQ": ref_dq, "dK": ref_dk, "dV": ref_dv}
+    for n in ("dQ", "dK", "dV"):
+        if np.linalg.norm(refs[n]) > 0:
+            assert e[n][1] <= bars["g_rel"], (n, e[n])
+    for h in range(cfg.H):
+        lim = LSE_FRZ_ABS if fz[h] else LSE_ORD_ABS
+        assert max_abs(got["l"][:, h], ref_l[:, h]) <= lim, (h, max_abs(got["l"][:, h], ref_l[:, h]))
+        if fz[h]:
+            # exact +0.0 for frozen heads' query/key gradients
+            assert np.all(got["dq"][:, h] == 0.0) and np.all(got["dk"][:, h] == 0.0)
+            assert not np.any(np.signbit(got["dq"][:, h])) and not np.any(np.signbit(got["dk"][:, h]))
+    for t in got.values():
+        assert np.all(np.isfinite(t))
+    return O, L, dq, dk, dv
+
+
+SMALL = [
+    CONFIGS["tiny"],
+    CONFIGS["pages_check_t129"],
+    CONFIGS["pages_check_t129"].with_(dtype="f32", name="pages-check_fp32"),
+    CONFIGS["pages_check_t129"].with_(frozen=(), name="pages-check_no-frozen"),
+    CONFIGS["pages_check_t129"].with_(frozen=(0, 1, 2, 3), name="pages-check_all-frozen"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_cases(B, cfg):
+    run_full_parity(B, cfg)
+
+
+@pytest.mark.parametrize("T", [1, 17, 64, 65, 127, 200, 257])
+def test_ragged_lengths(B, T):
+    cfg = CONFIGS["pages_check_t129"].with_(T=T, prior_len=T + 5, B=2, H=3, frozen=(1,), name=f"ragged_T{T}")
+    run_full_parity(B, cfg)
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+@pytest.mark.parametrize("mask", [(), (0,), (1, 3), (0, 1, 2, 3)])
+def test_head_dims_and_masks(B, D, mask):
+    cfg = CONFIGS["pages_check_t129"].with_(D=D, T=150, H=4, B=5, frozen=mask, qkv_scale=0.5,
+                                            name=f"D{D}_mask{''.join(map(str, mask))}")
+    run_full_parity(B, cfg)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_fp32_path(B, D):
+    cfg = CONFIGS["tiny"].with_(D=D, T=70, B=2, H=3, frozen=(2,), name=f"fp32_D{D}")
+    run_full_parity(B, cfg)
+
+
+def test_strided_views(B):
+    run_full_parity(B, CONFIGS["pages_check_t129"].with_(B=3, T=300, name="strided"), strided=True)
+
+
+def test_explicit_scale(B):
+    run_full_parity(B, CONFIGS["pages_check_t129"].with_(name="scale0.3"), scale=0.3)
+
+
+def test_frozen_qk_poison_and_determinism(B):
+    cfg = CONFIGS["pages_check_t129"].with_(T=260, B=4, name="poison")
+    r1 = run_full_parity(B, cfg)
+    r2 = run_full_parity(B, cfg, poison_frozen_qk=True)
+    r3 = run_full_parity(B, cfg)
+    for x, y, z in zip(r1, r2, r3):
+        assert torch.equal(x, z), "results must be bitwise reproducible"
+        fx = torch.nan_to_num(x)
+        fy = torch.nan_to_num(y)
+        assert torch.equal(fx, fy), "frozen heads' Q/K must not be read"
+
+
+def test_stage_events_do_not_change_results(B):
+    cfg = CONFIGS["pages_check_t129"].with_(T=333, B=2, name="events")
+    inp = make_inputs(cfg)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O1, L1 = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for e in evs:
+        e.record()
+    O2, L2 = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"], events=evs)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(L1, L2)
+    assert evs[0].elapsed_time(evs[2]) >= 0.0
+
+
+# --------------------------------------------------------------------------
+# Pattern entry points
+# --------------------------------------------------------------------------
+
+
+def test_lognorm_closed_form_and_gauge(B):
+    T = 32768
+    lam = 0.01
+    a = torch.zeros(1, T, dtype=torch.float32, device="cuda")
+    r = (-lam * torch.arange(T, dtype=torch.float64)).float().cuda()[None]
+    got = host(B.saf_pattern_lognorm(a, r, T))[0]
+    i = np.arange(T)
+    expect = np.log(-np.expm1(-lam * (i + 1))) - np.log(-np.expm1(-lam))
+    say(f"  geometric closed form max-abs {max_abs(got, expect):.3e}")
+    assert max_abs(got, expect) <= LSE_FRZ_ABS
+    rng = np.random.default_rng(1)
+    a0 = rng.standard_normal(T).astype(np.float32)
+    r0 = np.where(i < 8, 3.0, -0.01 * i).astype(np.float32)
+    a1 = (a0 + lam * i).astype(np.float32)
+    r1 = (r0 + lam * i).astype(np.float32)
+    L0 = host(B.saf_pattern_lognorm(torch.from_numpy(a0[None]).cuda(), torch.from_numpy(r0[None]).cuda(), T))[0]
+    L1 = host(B.saf_pattern_lognorm(torch.from_numpy(a1[None]).cuda(), torch.from_numpy(r1[None]).cuda(), T))[0]
+    # shifting a and r by lam*j and lam*d adds lam*i to log N; the oracle sees
+    # the same fp32-rounded shifted inputs
+    rows = np.unique(np.concatenate([np.arange(0, T, 97), [1, 7, 8, 9, T - 1]]))
+    zero_v = np.zeros((T, 1))
+    ref0 = oracle.frozen_rows_fwd(zero_v, a0, r0, rows)[1]
+    ref1 = oracle.frozen_rows_fwd(zero_v, a1, r1, rows)[1]
+    say(f"  peaked r: max-abs {max_abs(L0[rows], ref0):.3e}; shifted: {max_abs(L1[rows], ref1):.3e}")
+    assert max_abs(L0[rows], ref0) <= LSE_FRZ_ABS
+    assert max_abs(L1[rows], ref1) <= 4 * LSE_FRZ_ABS  # values reach ~330 here
+    assert np.all(np.isfinite(L1))
+    assert max_abs(L1 - L0, lam * i) <= 4 * LSE_FRZ_ABS
+
+
+@pytest.mark.parametrize("T,Tp", [(1, 1), (129, 192), (1000, 1000)])
+def test_pattern_dense_matches_oracle(B, T, Tp):
+    rng = np.random.default_rng(T)
+    a = rng.standard_normal(Tp).astype(np.float32)
+    r = (-0.05 * np.arange(Tp) + 0.5 * rng.standard_normal(Tp)).astype(np.float32)
+    W = host(B.saf_pattern_dense(torch.from_numpy(a).cuda(), torch.from_numpy(r).cuda(), T))
+    ref = oracle.frozen_pattern(a, r, T)
+    say(f"  T={T}: max-abs {max_abs(W, ref):.3e}")
+    assert max_abs(W, ref) <= 1e-5
+    assert np.all(np.triu(W, 1) == 0.0)
+    np.testing.assert_allclose(W.sum(axis=1), 1.0, atol=1e-5)
+
+
+def test_lognorm_special_patterns(B):
+    T = 300
+    i = np.arange(T)
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal(T).astype(np.float32)
+    ident = np.full(T, -np.inf, dtype=np.float32)
+    ident[0] = 0.0
+    window = np.where(i < 5, 0.0, -np.inf).astype(np.float32)
+    got = host(B.saf_pattern_lognorm(torch.from_numpy(np.stack([a, np.zeros(T, np.float32)])).cuda(),
+                                     torch.from_numpy(np.stack([ident, window])).cuda(), T))
+    assert max_abs(got[0], a) <= 1e-6  # identity pattern: log N(i) = a[i]
+    assert max_abs(got[1], np.log(np.minimum(i + 1, 5))) <= 1e-6
+
+
+# --------------------------------------------------------------------------
+# Workload shapes: sampled heads / rows against the oracle
+# --------------------------------------------------------------------------
+
+SAMPLES = {
+    "gpt2_124m_4k_25pct": [(7, 0), (3, 10)],
+    "gpt2_124m_4k_50pct_interleaved": [(0, 0), (5, 11)],
+    "1b_8k_rank_share": [(1, 3), (0, 15)],
+}
+
+
+@pytest.mark.parametrize("key", list(SAMPLES))
+def test_workload_sampled_heads(B, key):
+    cfg = CONFIGS[key]
+    say(f"workload {cfg.name}")
+    inp = make_inputs(cfg)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    dq, dk, dv = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    # properties at full size
+    for h in range(cfg.H):
+        if fz[h]:
+            assert int(torch.count_nonzero(dq[:, h])) == 0 and int(torch.count_nonzero(dk[:, h])) == 0
+    for t in (O, L, dq, dk, dv):
+        assert bool(torch.isfinite(t.float()).all())
+    s = 1.0 / np.sqrt(cfg.D)
+    for b, h in SAMPLES[key]:
+        say(f"  head b={b} h={h} frozen={fz[h]}")
+        if fz[h]:
+            ro, rl = oracle.frozen_head_fwd(inp.v[b, h], inp.a[h], inp.r[h])
+            rdv = oracle.frozen_head_bwd(inp.do[b, h], inp.a[h], inp.r[h])
+            rdq = rdk = None
+        else:
+            ro, rl = oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], s)
+            rdq, rdk, rdv = oracle.ordinary_head_bwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], s)
+        _check_head(f"b{b}h{h}", cfg, host(O[b, h]), ro, host(L[b, h]), rl, fz[h])
+        for n, g, rr in (("dQ", dq, rdq), ("dK", dk, rdk), ("dV", dv, rdv)):
+            if rr is None:
+                continue
+            e = rel_l2(host(g[b, h]), rr)
+            say(f"    {n} rel-L2 {e:.3e}")
+            assert e <= BF16_GRAD_RELL2, (n, e)
+
+
+def test_workload_prefill_32k_sampled_rows(B):
+    cfg = CONFIGS["prefill_32k"]
+    say(f"workload {cfg.name}")
+    inp = make_inputs(cfg)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O.float()).all()) and bool(torch.isfinite(L).all())
+    T = cfg.T
+    rows = np.unique(np.concatenate([[0, 1, 7, 8, 9, 127, 128, 4095, T - 2, T - 1],
+                                     np.random.default_rng(0).integers(0, T, 40)]))
+    s = 1.0 / np.sqrt(cfg.D)
+    for h in (0, 5, 9, 11):
+        if fz[h]:
+            ro, rl = oracle.frozen_rows_fwd(inp.v[0, h], inp.a[h], inp.r[h], rows)
+        else:
+            ro, rl = oracle.ordinary_rows_fwd(inp.q[0, h], inp.k[0, h], inp.v[0, h], s, rows)
+        _check_head(f"h{h} rows", cfg, host(O[0, h])[rows], ro, host(L[0, h])[rows], rl, fz[h])
+    # log N of one frozen head on every 61st row
+    h = 10
+    rows = np.arange(0, T, 61)
+    rl = oracle.frozen_rows_fwd(np.zeros((T, 1)), inp.a[h], inp.r[h], rows)[1]
+    e = max_abs(host(L[0, h])[rows], rl)
+    say(f"  h{h} log N on {len(rows)} rows max-abs {e:.3e}")
+    assert e <= LSE_FRZ_ABS
