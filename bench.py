@@ -1,0 +1,230 @@
+"""Throughput of the SAF hybrid attention layer (forward + backward) on one GPU.
+
+A step is one forward and one backward of the hybrid layer over one batch of
+seeded synthetic inputs resident in HBM (workload: the 124M GPT layer shape,
+B=8, H=12 with the last 3 heads frozen, T=4096, d=64, bf16).  The headline
+value is algorithmic TFLOP/s under the FlashAttention-2 counting convention:
+per causal pair, ordinary heads count 4d (forward) + 10d (backward) flops and
+frozen heads 2d + 2d.
+
+Prints ONE JSON line.  Also reports, for the dominant kernel, its roofline
+position from HIP events that the library records around each of its kernels
+on the launch stream, and the float64 CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def pairs(T: int) -> int:
+    return T * (T + 1) // 2
+
+
+def flops(cfg, n_ord=None, n_frz=None, B=None):
+    """Algorithmic flops of one forward and one backward (FA2 convention),
+    split over the kernels that perform them."""
+    P = pairs(cfg.T)
+    d = cfg.D
+    B = cfg.B if B is None else B
+    n_frz = len(cfg.frozen) if n_frz is None else n_frz
+    n_ord = cfg.H - n_frz if n_ord is None else n_ord
+    f = {
+        "fwd_ord": P * d * 4 * B * n_ord,     # S = QK^T, O = PV
+        "fwd_frz": P * d * 2 * B * n_frz,     # O = WV
+        "bwd_kv_ord": P * d * 8 * B * n_ord,  # S, dP recomputed once; dV, dK
+        "bwd_kv_frz": P * d * 2 * B * n_frz,  # dV = W^T dO
+        "bwd_q": P * d * 2 * B * n_ord,       # dQ
+    }
+    f["fwd"] = f["fwd_ord"] + f["fwd_frz"]
+    f["bwd"] = f["bwd_kv_ord"] + f["bwd_kv_frz"] + f["bwd_q"]
+    f["total"] = f["fwd"] + f["bwd"]
+    return f
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 20.0):
+    """Time the float64 oracle on whole heads of the workload (host cores)."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    s = 1.0 / np.sqrt(cfg.D)
+    fz = [int(x) for x in inp.frozen]
+    # alternate ordinary / frozen heads of batch element 0 until the budget is used
+    order = []
+    ords = [h for h in range(cfg.H) if not fz[h]]
+    frzs = [h for h in range(cfg.H) if fz[h]]
+    for x in range(max(len(ords), len(frzs))):
+        if x < len(ords):
+            order.append(ords[x])
+        if x < len(frzs):
+            order.append(frzs[x])
+    done_ord = done_frz = 0
+    t0 = time.perf_counter()
+    for h in order:
+        if fz[h]:
+            oracle.frozen_head_fwd(inp.v[0, h], inp.a[h], inp.r[h])
+            if inp.do is not None:
+                oracle.frozen_head_bwd(inp.do[0, h], inp.a[h], inp.r[h])
+            done_frz += 1
+        else:
+            oracle.ordinary_head_fwd(inp.q[0, h], inp.k[0, h], inp.v[0, h], s)
+            if inp.do is not None:
+                oracle.ordinary_head_bwd(inp.q[0, h], inp.k[0, h], inp.v[0, h], inp.do[0, h], s)
+            done_ord += 1
+        if time.perf_counter() - t0 >= budget_s and done_ord and done_frz:
+            break
+    dt = time.perf_counter() - t0
+    f = flops(cfg, n_ord=done_ord, n_frz=done_frz, B=1)
+    fl = f["total"] if inp.do is not None else f["fwd"]
+    return {
+        "value": fl / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"float64 dense oracle, fwd+bwd of {done_ord} ordinary + {done_frz} frozen whole heads "
+                  f"(b=0, T={cfg.T}, d={cfg.D}) in {dt:.1f} s; value = their algorithmic flops / time",
+        "seconds": round(dt, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gpt2_124m_4k_25pct")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is not built "
+                                   "(--gpus must be 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fixed_pattern_hybrid_amd import binding as B
+    from synth import CONFIGS, make_inputs
+
+    cfg = CONFIGS[args.config]
+    inp = make_inputs(cfg)
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dt)  # noqa: E731
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    do = dev(inp.do) if inp.do is not None else None
+    a, r = torch.from_numpy(inp.a).cuda(), torch.from_numpy(inp.r).cuda()
+    fz = [int(x) for x in inp.frozen]
+    Bn, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
+    o = torch.empty_like(v)
+    lse = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
+    dq, dk, dv = torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)
+    prm = B.Params(v, fz, a.shape[1])
+    ws = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
+    has_frz = any(fz)
+    has_ord = not all(fz)
+    names_f = (["lognorm"] if has_frz else []) + (["fwd_ord"] if has_ord else []) + (["fwd_frz"] if has_frz else [])
+    names_b = ["bwd_pre"] + (["bwd_kv_ord"] if has_ord else []) + (["bwd_kv_frz"] if has_frz else []) \
+        + (["bwd_q"] if has_ord else [])
+    n_fwd_ev = len(names_f) + 1
+    n_bwd_ev = len(names_b) + 1
+    stream = torch.cuda.current_stream()
+
+    def mk_events(n):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in evs:
+            e.record(stream)  # creates the underlying HIP event
+        return evs
+
+    def step(fe=None, be=None):
+        B.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=o, lse=lse, stream=stream, events=fe)
+        if do is not None:
+            B.saf_hybrid_attn_bwd(q, k, v, o, do, lse, fz, a, r, dq=dq, dk=dk, dv=dv, workspace=ws,
+                                  stream=stream, events=be)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    fevs = [mk_events(n_fwd_ev) for _ in range(K)]
+    bevs = [mk_events(n_bwd_ev) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(K):
+        step(fevs[s], bevs[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = t_start.elapsed_time(t_end) / K
+
+    # per-kernel durations from the library's stage events
+    per = {n: [] for n in names_f + names_b}
+    for s in range(K):
+        for x, n in enumerate(names_f):
+            per[n].append(fevs[s][x].elapsed_time(fevs[s][x + 1]))
+        if do is not None:
+            for x, n in enumerate(names_b):
+                per[n].append(bevs[s][x].elapsed_time(bevs[s][x + 1]))
+    kern_ms = {n: float(np.mean(v_)) for n, v_ in per.items() if v_}
+
+    f = flops(cfg)
+    total = f["total"] if do is not None else f["fwd"]
+    value = total / (ms * 1e-3) / 1e12
+    tokens = Bn * T / (ms * 1e-3)
+    # dominant kernel and its algorithmic flops per launch
+    dom = max(kern_ms, key=kern_ms.get)
+    dom_flops = f.get(dom)
+    roof = None
+    if dom_flops is not None:
+        ach = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "kernel_ms": round(kern_ms[dom], 4)}
+    out = {
+        "metric": "hybrid-attn fwd+bwd TFLOP/s & MFMA util, 124M/4K shape, 25% heads frozen",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "B": Bn, "H": H, "T": T, "D": D, "frozen_heads": list(cfg.frozen),
+                   "pass": "fwd+bwd" if do is not None else "fwd"},
+        "mfma_util": round(value / PEAK_BF16_TFLOPS, 4),
+        "tokens_per_s": round(tokens, 1),
+        "kernel_ms": {n: round(x, 4) for n, x in kern_ms.items()},
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

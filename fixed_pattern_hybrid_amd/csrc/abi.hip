@@ -7,10 +7,6 @@
 #include <cmath>
 #include <cstring>
 
-namespace saf {
-hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
-}
-
 namespace {
 
 using saf::BwdArgs;
@@ -191,10 +187,19 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
     if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;
     if (stg.mark() != hipSuccess) return SAF_EHIP;
   }
-  hipError_t e = (p->dtype == SAF_BF16) ? saf::launch_fwd_bf16(args, p->D, stream)
-                                        : saf::launch_fwd_f32(args, p->D, stream);
-  if (e != hipSuccess) return SAF_EHIP;
-  if (stg.mark() != hipSuccess) return SAF_EHIP;
+  if (p->dtype == SAF_BF16) {
+    if (n_ord > 0) {
+      if (saf::launch_fwd_ord_bf16(args, p->D, stream) != hipSuccess) return SAF_EHIP;
+      if (stg.mark() != hipSuccess) return SAF_EHIP;
+    }
+    if (n_frz > 0) {
+      if (saf::launch_fwd_frz_bf16(args, p->D, stream) != hipSuccess) return SAF_EHIP;
+      if (stg.mark() != hipSuccess) return SAF_EHIP;
+    }
+  } else {
+    if (saf::launch_fwd_f32(args, p->D, stream) != hipSuccess) return SAF_EHIP;
+    if (stg.mark() != hipSuccess) return SAF_EHIP;
+  }
   return SAF_OK;
 }
 
@@ -244,17 +249,34 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   args.n_frz = n_frz;
   fill_heads(p, args.ord_heads, args.frz_heads, args.is_frozen);
 
-  const bool bf = p->dtype == SAF_BF16;
   Stages stg{p, stream};
   if (stg.mark() != hipSuccess) return SAF_EHIP;
-  hipError_t e = bf ? saf::launch_bwd_pre_bf16(args, p->D, stream)
-                    : saf::launch_bwd_pre_f32(args, p->D, stream);
-  if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-  e = bf ? saf::launch_bwd_kv_bf16(args, p->D, stream) : saf::launch_bwd_kv_f32(args, p->D, stream);
-  if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-  if (n_ord > 0) {
-    e = bf ? saf::launch_bwd_q_bf16(args, p->D, stream) : saf::launch_bwd_q_f32(args, p->D, stream);
+  hipError_t e;
+  if (p->dtype == SAF_BF16) {
+    // delta + zero frozen dQ/dK, key-block passes, query-block pass
+    e = saf::launch_bwd_pre_bf16(args, p->D, stream);
     if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    if (n_ord > 0) {
+      e = saf::launch_bwd_kv_ord_bf16(args, p->D, stream);
+      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    }
+    if (n_frz > 0) {
+      e = saf::launch_bwd_kv_frz_bf16(args, p->D, stream);
+      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    }
+    if (n_ord > 0) {
+      e = saf::launch_bwd_q_bf16(args, p->D, stream);
+      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    }
+  } else {
+    e = saf::launch_bwd_pre_f32(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    e = saf::launch_bwd_kv_f32(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    if (n_ord > 0) {
+      e = saf::launch_bwd_q_f32(args, p->D, stream);
+      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    }
   }
   return SAF_OK;
 }

@@ -108,8 +108,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
 // Key-block pass, ordinary head (b, h, kb).
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem) {
+__global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
   using C = BwdCfg<D>;
+  SAF_DYN_LDS(smem);
+  const int per_k = A.B * A.n_ord;
+  const int kb = blockIdx.x / per_k;  // key block 0 has the most queries: first
+  const int rem = blockIdx.x - kb * per_k;
+  const int b = rem / A.n_ord;
+  const int h = A.ord_heads[rem - b * A.n_ord];
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
@@ -138,17 +144,16 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
     }
   }
 
-  __bf16* Qs[2] = {smem, smem + C::TILE};
-  __bf16* Os[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
-  float* fb = (float*)(smem + 4 * C::TILE);
-  float* Ls[2] = {fb, fb + kKvBM};
-  float* Ds[2] = {fb + 2 * kKvBM, fb + 3 * kKvBM};
+  // LDS: Q[buf] at buf*TILE, dO[buf] at (2+buf)*TILE, then lse2[buf], delta[buf]
+  lds_f32* fb = (lds_f32*)(smem + 4 * C::TILE);
 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
 
   TileStage<D, kKvBM, kThreads> qst, ost;
-  auto stage_vec = [&](int i0, float* ls, float* ds) {
+  auto stage_vec = [&](int i0, int buf) {
+    lds_f32* ls = fb + buf * kKvBM;
+    lds_f32* ds = fb + (2 + buf) * kKvBM;
     for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
       const int i = i0 + x;
       ls[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();  // padding rows: P = 0
@@ -158,9 +163,9 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
   if (qt0 < nqt) {
     qst.load(qg, A.q.st, qt0 * kKvBM, T);
     ost.load(dog, A.dout.st, qt0 * kKvBM, T);
-    qst.store(Qs[0], C::PITCH);
-    ost.store(Os[0], C::PITCH);
-    stage_vec(qt0 * kKvBM, Ls[0], Ds[0]);
+    qst.store(smem, C::PITCH);
+    ost.store(smem + 2 * C::TILE, C::PITCH);
+    stage_vec(qt0 * kKvBM, 0);
   }
   __syncthreads();
 
@@ -180,10 +185,10 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
       qst.load(qg, A.q.st, i0 + kKvBM, T);
       ost.load(dog, A.dout.st, i0 + kKvBM, T);
     }
-    const __bf16* Q = Qs[bi];
-    const __bf16* O = Os[bi];
-    const float* ls = Ls[bi];
-    const float* ds = Ds[bi];
+    const lds_bf16* Q = smem + bi * C::TILE;
+    const lds_bf16* O = smem + (2 + bi) * C::TILE;
+    const lds_f32* ls = fb + bi * kKvBM;
+    const lds_f32* ds = fb + (2 + bi) * kKvBM;
     if (i0 + kKvBM - 1 >= wk_lo) {
       f32x16 s[2], dp[2];
 #pragma unroll
@@ -202,8 +207,8 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ib = 32 * c + 8 * q4 + 4 * hl;  // first of 4 consecutive tile rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + ib);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(ds + ib);
+          const f32x4 l4 = lds_read_f4(ls + ib);
+          const f32x4 d4 = lds_read_f4(ds + ib);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
@@ -226,9 +231,9 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
       }
     }
     if (more) {
-      qst.store(Qs[bi ^ 1], C::PITCH);
-      ost.store(Os[bi ^ 1], C::PITCH);
-      stage_vec(i0 + kKvBM, Ls[bi ^ 1], Ds[bi ^ 1]);
+      qst.store(smem + (bi ^ 1) * C::TILE, C::PITCH);
+      ost.store(smem + (2 + (bi ^ 1)) * C::TILE, C::PITCH);
+      stage_vec(i0 + kKvBM, bi ^ 1);
     }
     __syncthreads();
   }
@@ -240,9 +245,15 @@ __device__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, __bf16* smem
 // Key-block pass, frozen head (h, kb, batch group): dV = W^T dO.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem) {
+__global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
   using C = BwdCfg<D>;
   constexpr int G = C::G;
+  SAF_DYN_LDS(smem);
+  const int per_k = A.n_frz * A.n_groups;
+  const int kb = blockIdx.x / per_k;
+  const int rem = blockIdx.x - kb * per_k;
+  const int h = A.frz_heads[rem / A.n_groups];
+  const int grp = rem % A.n_groups;
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
@@ -256,10 +267,9 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
   const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
   const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, same for every b
 
-  __bf16* Os[2] = {smem, smem + G * C::TILE};
-  float* fb = (float*)(smem + 2 * G * C::TILE);
-  float* Zs[2] = {fb, fb + kKvBM + C::BAND};
-  float* Rs[2] = {fb + kKvBM, fb + 2 * kKvBM + C::BAND};
+  // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and the r band[BAND]
+  lds_f32* fb = (lds_f32*)(smem + 2 * G * C::TILE);
+  constexpr int FSTRIDE = kKvBM + C::BAND;
 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
@@ -273,13 +283,15 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
       ost[gb].load(g, A.dout.st, i0, T);
     }
   };
-  auto store_do = [&](__bf16* dst) {
+  auto store_do = [&](int buf) {
 #pragma unroll
-    for (int gb = 0; gb < G; ++gb) ost[gb].store(dst + gb * C::TILE, C::PITCH);
+    for (int gb = 0; gb < G; ++gb) ost[gb].store(smem + (buf * G + gb) * C::TILE, C::PITCH);
   };
   // z2 = log N (log2 units) of the tile rows; r band over offsets
   // [i0 - k0 - (BN-1), i0 + BM - 1 - k0].
-  auto stage_pattern = [&](int i0, float* zs, float* rs) {
+  auto stage_pattern = [&](int i0, int buf) {
+    lds_f32* zs = fb + buf * FSTRIDE;
+    lds_f32* rs = zs + kKvBM;
     for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
       const int i = i0 + x;
       zs[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();
@@ -293,8 +305,8 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
 
   if (qt0 < nqt) {
     load_do(qt0 * kKvBM);
-    store_do(Os[0]);
-    stage_pattern(qt0 * kKvBM, Zs[0], Rs[0]);
+    store_do(0);
+    stage_pattern(qt0 * kKvBM, 0);
   }
   __syncthreads();
 
@@ -309,9 +321,8 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
     if (more) load_do(i0 + kKvBM);
-    const __bf16* O = Os[bi];
-    const float* zs = Zs[bi];
-    const float* rs = Rs[bi];
+    const lds_f32* zs = fb + bi * FSTRIDE;
+    const lds_f32* rs = zs + kKvBM;
     if (i0 + kKvBM - 1 >= wk_lo) {
       // band index of (i, j): (i - i0) - (j - k0) + BN - 1
       const int xj = (kKvBN - 1) - (j - k0);
@@ -328,13 +339,13 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            dva[gb][db] = mfma32(lds_frag_tr(O + gb * C::TILE, C::PITCH, 16 * st, 32 * db), wf,
-                                 dva[gb][db]);
+            dva[gb][db] = mfma32(lds_frag_tr(smem + (bi * G + gb) * C::TILE, C::PITCH, 16 * st, 32 * db),
+                                 wf, dva[gb][db]);
       }
     }
     if (more) {
-      store_do(Os[bi ^ 1]);
-      stage_pattern(i0 + kKvBM, Zs[bi ^ 1], Rs[bi ^ 1]);
+      store_do(bi ^ 1);
+      stage_pattern(i0 + kKvBM, bi ^ 1);
     }
     __syncthreads();
   }
@@ -343,30 +354,13 @@ __device__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, __bf16* smem
     if (gb < nb) store_rows_t<D>(A.dv, b0 + gb, h, j, T, dva[gb], 1.f);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_kv_kernel(BwdArgs A) {
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-  const int per_k = A.B * A.n_ord + A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / per_k;  // key block 0 has the most queries: first
-  const int rem = blockIdx.x - kb * per_k;
-  if (rem < A.B * A.n_ord) {
-    const int b = rem / A.n_ord;
-    kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], kb, smem);
-  } else {
-    const int f = rem - A.B * A.n_ord;
-    kv_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, kb, smem);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Query-block pass, ordinary head (b, h, qb): dQ = s dS K.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   using C = BwdCfg<D>;
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
+  SAF_DYN_LDS(smem);
   const int per_q = A.B * A.n_ord;
   const int qrank = blockIdx.x / per_q;
   const int rem = blockIdx.x - qrank * per_q;
@@ -400,16 +394,14 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   const float l2 = (i < T) ? A.lse[rowv] * kLog2e : __builtin_inff();
   const float dl = (i < T) ? A.delta[rowv] : 0.f;
 
-  __bf16* Ks[2] = {smem, smem + C::TILE};
-  __bf16* Vs[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
   const int last_key = min(q0 + kQBM, T) - 1;
   const int ntiles = last_key / kQBN + 1;
 
   TileStage<D, kQBN, kThreads> kst, vst;
   kst.load(kg, A.k.st, 0, T);
   vst.load(vg, A.v.st, 0, T);
-  kst.store(Ks[0], C::PITCH);
-  vst.store(Vs[0], C::PITCH);
+  kst.store(smem, C::PITCH);
+  vst.store(smem + 2 * C::TILE, C::PITCH);
   __syncthreads();
 
   f32x16 dqa[C::NDB];
@@ -424,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
       kst.load(kg, A.k.st, j0 + kQBN, T);
       vst.load(vg, A.v.st, j0 + kQBN, T);
     }
-    const __bf16* K = Ks[t & 1];
-    const __bf16* V = Vs[t & 1];
+    const lds_bf16* K = smem + (t & 1) * C::TILE;
+    const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
     if (j0 <= wq_hi) {
       f32x16 s[2], dp[2];
 #pragma unroll
@@ -460,8 +452,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
       }
     }
     if (more) {
-      kst.store(Ks[(t + 1) & 1], C::PITCH);
-      vst.store(Vs[(t + 1) & 1], C::PITCH);
+      kst.store(smem + ((t + 1) & 1) * C::TILE, C::PITCH);
+      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE, C::PITCH);
     }
     __syncthreads();
   }
@@ -475,21 +467,34 @@ hipError_t launch_pre_d(const BwdArgs& args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int D>
-hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
+hipError_t launch_kv_d(BwdArgs args, hipStream_t stream, int which) {
   using C = BwdCfg<D>;
+  static_assert(C::kv_ord_lds <= 160 * 1024 && C::kv_frz_lds <= 160 * 1024, "LDS budget");
+  static const hipError_t a1 = set_lds(bwd_kv_ord_kernel<D>, C::kv_ord_lds);
+  static const hipError_t a2 = set_lds(bwd_kv_frz_kernel<D>, C::kv_frz_lds);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
-  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
-  if (grid <= 0) return hipSuccess;
-  static_assert(C::kv_lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(bwd_kv_kernel<D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kv_lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_lds, stream,
-                     args);
+  if (which == 0) {
+    const int64_t grid = (int64_t)args.B * args.n_ord * args.nkb;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_kv_ord_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_ord_lds,
+                       stream, args);
+  } else {
+    const int64_t grid = (int64_t)args.n_frz * args.n_groups * args.nkb;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_kv_frz_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_frz_lds,
+                       stream, args);
+  }
   return hipGetLastError();
 }
 
@@ -499,9 +504,7 @@ hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
   args.nqb = (args.T + kQBM - 1) / kQBM;
   const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
   if (grid <= 0) return hipSuccess;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(bwd_q_kernel<D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::q_lds);
+  static const hipError_t attr = set_lds(bwd_q_kernel<D>, C::q_lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(bwd_q_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::q_lds, stream,
                      args);
@@ -519,13 +522,20 @@ hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream) {
   }
 }
 
-hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+static hipError_t launch_kv_which(const BwdArgs& args, int D, hipStream_t stream, int which) {
   switch (D) {
-    case 64: return launch_kv_d<64>(args, stream);
-    case 96: return launch_kv_d<96>(args, stream);
-    case 128: return launch_kv_d<128>(args, stream);
+    case 64: return launch_kv_d<64>(args, stream, which);
+    case 96: return launch_kv_d<96>(args, stream, which);
+    case 128: return launch_kv_d<128>(args, stream, which);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_bwd_kv_ord_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+  return launch_kv_which(args, D, stream, 0);
+}
+hipError_t launch_bwd_kv_frz_bf16(const BwdArgs& args, int D, hipStream_t stream) {
+  return launch_kv_which(args, D, stream, 1);
 }
 
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream) {

@@ -1,22 +1,25 @@
-// Mixed-head forward of the SAF hybrid attention layer, bf16, gfx950.
+// Forward of the SAF hybrid attention layer, bf16, gfx950.
 //
-// One launch covers every head ("When Can Attention Heads Be Statically
-// Defined?", Section 3.3 "Fused computation" and Appendix D.2): each program
-// reads the head-state flag of its head and runs either
-//   * an ordinary program (b, h, query block): online-softmax tiling of
-//     causal attention (Appendix A.1, Equations 5-7), or
-//   * a frozen program (h, query block, group of batch elements): each causal
-//     tile of the compact pattern (Section 3.2, Equation 3) is rebuilt in
-//     registers once from a, r and the precomputed row normalisers, then
-//     multiplied with the value tiles of every batch element in the group.
-//     The weights do not depend on the batch index, so rebuilding them once
-//     per group divides the exp work by the group size.
-// Outputs are written in the original head order.
+// Head kinds ("When Can Attention Heads Be Statically Defined?", Section 3.3
+// "Fused computation" and Appendix D.2):
+//   * ordinary head, one program per (b, h, query block): online-softmax
+//     tiling of causal attention (Appendix A.1, Equations 5-7);
+//   * frozen head, one program per (h, query block, group of batch
+//     elements): each causal tile of the compact pattern (Section 3.2,
+//     Equation 3) is rebuilt in registers once from a, r and the precomputed
+//     row normalisers, then multiplied with the value tiles of every batch
+//     element of the group.  The weights do not depend on the batch index,
+//     so one rebuild serves the whole group.
+// Outputs are written in the original head order.  The two kinds run as two
+// kernels on the caller's stream: on gfx950 registers are allocated per
+// kernel, and the frozen programs' per-batch accumulators would otherwise
+// lower the occupancy of the ordinary programs.
 //
 // Work layout: 4 waves, 32 queries per wave, key tiles of 64.  Products are
 // computed transposed (S^T = K Q^T, O^T = V^T P^T) so that every lane owns
 // one query: row max, row sum and rescaling stay in the lane, and the C
-// registers of S^T convert directly into the B operand of the second product.
+// registers of S^T convert directly into the B operand of the second product
+// (V^T comes from LDS through transposing reads).
 #include "saf_internal.h"
 #include "saf_tile.h"
 
@@ -37,7 +40,6 @@ struct FwdCfg {
   static constexpr int BAND = kBM + kBN;       // r band length (BM + BN - 1, padded)
   static constexpr size_t ord_lds = size_t(2) * 2 * TILE * 2;
   static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * (kBN + BAND) * 4;
-  static constexpr size_t lds = ord_lds > frz_lds ? ord_lds : frz_lds;
 };
 
 template <int D>
@@ -62,11 +64,20 @@ __device__ __forceinline__ void store_out_rows(const TensorRef& o, int b, int h,
 }
 
 // ---------------------------------------------------------------------------
-// Ordinary head: causal softmax attention with an online row maximum.
+// Ordinary heads: causal softmax attention with an online row maximum.
+// Grid: nqb * B * n_ord programs, longest query blocks first.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* smem) {
+__global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
   using C = FwdCfg<D>;
+  SAF_DYN_LDS(smem);
+  const int per_q = A.B * A.n_ord;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
+  const int qb = A.nqb - 1 - qrank;
+  const int b = rem / A.n_ord;
+  const int h = A.ord_heads[rem - b * A.n_ord];
+
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int q0 = qb * kBM;
@@ -88,17 +99,15 @@ __device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* sme
     }
   }
 
-  __bf16* Ks[2] = {smem, smem + C::TILE};
-  __bf16* Vs[2] = {smem + 2 * C::TILE, smem + 3 * C::TILE};
-
+  // LDS: K[buf], V[buf] at (2*kind + buf) * TILE
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
   TileStage<D, kBN, kThreads> kst, vst;
   kst.load(kg, A.k.st, 0, T);
   vst.load(vg, A.v.st, 0, T);
-  kst.store(Ks[0], C::PITCH);
-  vst.store(Vs[0], C::PITCH);
+  kst.store(smem, C::PITCH);
+  vst.store(smem + 2 * C::TILE, C::PITCH);
   __syncthreads();
 
   f32x16 oacc[C::NDB];
@@ -114,8 +123,8 @@ __device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* sme
       kst.load(kg, A.k.st, j0 + kBN, T);
       vst.load(vg, A.v.st, j0 + kBN, T);
     }
-    const __bf16* K = Ks[t & 1];
-    const __bf16* V = Vs[t & 1];
+    const lds_bf16* K = smem + (t & 1) * C::TILE;
+    const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
     if (j0 <= wq_hi) {
       f32x16 s[2];
 #pragma unroll
@@ -170,8 +179,8 @@ __device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* sme
       }
     }
     if (more) {
-      kst.store(Ks[(t + 1) & 1], C::PITCH);
-      vst.store(Vs[(t + 1) & 1], C::PITCH);
+      kst.store(smem + ((t + 1) & 1) * C::TILE, C::PITCH);
+      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE, C::PITCH);
     }
     __syncthreads();
   }
@@ -182,12 +191,21 @@ __device__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, __bf16* sme
 }
 
 // ---------------------------------------------------------------------------
-// Frozen head: W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
+// Frozen heads: W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
+// Grid: nqb * n_frz * n_groups programs, longest query blocks first.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* smem) {
+__global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
   using C = FwdCfg<D>;
   constexpr int G = C::G;
+  SAF_DYN_LDS(smem);
+  const int per_q = A.n_frz * A.n_groups;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
+  const int qb = A.nqb - 1 - qrank;
+  const int h = A.frz_heads[rem / A.n_groups];
+  const int grp = rem % A.n_groups;
+
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int q0 = qb * kBM;
@@ -196,10 +214,9 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
   const int b0 = grp * G;
   const int nb = min(G, A.B - b0);
 
-  __bf16* Vs[2] = {smem, smem + G * C::TILE};
-  float* fbase = (float*)(smem + 2 * G * C::TILE);
-  float* As[2] = {fbase, fbase + kBN + C::BAND};
-  float* Rs[2] = {fbase + kBN, fbase + 2 * kBN + C::BAND};
+  // LDS: V tiles [buf][gb], then per buffer a2[kBN] and the r band[BAND]
+  lds_f32* fbase = (lds_f32*)(smem + 2 * G * C::TILE);
+  constexpr int FSTRIDE = kBN + C::BAND;
 
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
@@ -208,8 +225,9 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
-  // a (log2 units) for tile keys and the reversed-free r band of the tile.
-  auto stage_pattern = [&](int j0, float* as, float* rs) {
+  // a (log2 units) for the tile keys and r over offsets of the tile's band.
+  auto stage_pattern = [&](int j0, lds_f32* as) {
+    lds_f32* rs = as + kBN;
     for (int x = threadIdx.x; x < kBN; x += kThreads) {
       const int j = j0 + x;
       as[x] = (j < T) ? arow[j] * kLog2e : kNegInf;
@@ -230,14 +248,14 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
       vst[gb].load(vg, A.v.st, j0, T);
     }
   };
-  auto store_v = [&](__bf16* dst) {
+  auto store_v = [&](int buf) {
 #pragma unroll
-    for (int gb = 0; gb < G; ++gb) vst[gb].store(dst + gb * C::TILE, C::PITCH);
+    for (int gb = 0; gb < G; ++gb) vst[gb].store(smem + (buf * G + gb) * C::TILE, C::PITCH);
   };
 
   load_v(0);
-  stage_pattern(0, As[0], Rs[0]);
-  store_v(Vs[0]);
+  stage_pattern(0, fbase);
+  store_v(0);
   __syncthreads();
 
   f32x16 oacc[G][C::NDB];
@@ -250,9 +268,9 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
     if (more) load_v(j0 + kBN);
-    const __bf16* V = Vs[t & 1];
-    const float* as = As[t & 1];
-    const float* rs = Rs[t & 1];
+    const int buf = t & 1;
+    const lds_f32* as = fbase + buf * FSTRIDE;
+    const lds_f32* rs = as + kBN;
     if (j0 <= wq_hi) {
       // band index of (i, j): (i - q0) - (j - j0) + BN - 1
       const int xi = (i - q0) + kBN - 1;
@@ -269,13 +287,13 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            oacc[gb][db] = mfma32(lds_frag_tr(V + gb * C::TILE, C::PITCH, 16 * st, 32 * db), wf,
-                                  oacc[gb][db]);
+            oacc[gb][db] = mfma32(lds_frag_tr(smem + (buf * G + gb) * C::TILE, C::PITCH, 16 * st, 32 * db),
+                                  wf, oacc[gb][db]);
       }
     }
     if (more) {
-      store_v(Vs[(t + 1) & 1]);
-      stage_pattern(j0 + kBN, As[(t + 1) & 1], Rs[(t + 1) & 1]);
+      store_v(buf ^ 1);
+      stage_pattern(j0 + kBN, fbase + (buf ^ 1) * FSTRIDE);
     }
     __syncthreads();
   }
@@ -285,53 +303,51 @@ __device__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, __bf16* sme
     if (gb < nb) store_out_rows<D>(A.o, b0 + gb, h, i, T, oacc[gb], 1.f);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs A) {
-  extern __shared__ __align__(16) char smem_raw[];
-  __bf16* smem = reinterpret_cast<__bf16*>(smem_raw);
-  const int per_q = A.B * A.n_ord + A.n_frz * A.n_groups;
-  const int qrank = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qrank * per_q;
-  const int qb = A.nqb - 1 - qrank;  // longest query blocks first
-  if (rem < A.B * A.n_ord) {
-    const int b = rem / A.n_ord;
-    const int h = A.ord_heads[rem - b * A.n_ord];
-    fwd_ordinary<D>(A, b, h, qb, smem);
-  } else {
-    const int f = rem - A.B * A.n_ord;
-    const int h = A.frz_heads[f / A.n_groups];
-    fwd_frozen<D>(A, h, f % A.n_groups, qb, smem);
-  }
+template <typename K>
+hipError_t set_lds(K kernel, size_t bytes) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
 template <int D>
-hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
+hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream, int which) {
   using C = FwdCfg<D>;
+  static_assert(C::ord_lds <= 160 * 1024 && C::frz_lds <= 160 * 1024, "LDS budget");
+  static const hipError_t a1 = set_lds(fwd_ord_kernel<D>, C::ord_lds);
+  static const hipError_t a2 = set_lds(fwd_frz_kernel<D>, C::frz_lds);
+  if (a1 != hipSuccess) return a1;
+  if (a2 != hipSuccess) return a2;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nqb = (args.T + kBM - 1) / kBM;
-  const int per_q = args.B * args.n_ord + args.n_frz * args.n_groups;
-  const int64_t grid = (int64_t)per_q * args.nqb;
-  if (grid <= 0) return hipSuccess;
-  static_assert(C::lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(fwd_bf16_kernel<D>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::lds, stream,
-                     args);
+  if (which == 0) {
+    const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_ord_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::ord_lds, stream, args);
+  } else {
+    const int64_t grid = (int64_t)args.n_frz * args.n_groups * args.nqb;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fwd_frz_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::frz_lds, stream, args);
+  }
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_which(const FwdArgs& args, int D, hipStream_t stream, int which) {
+  switch (D) {
+    case 64: return launch_fwd_d<64>(args, stream, which);
+    case 96: return launch_fwd_d<96>(args, stream, which);
+    case 128: return launch_fwd_d<128>(args, stream, which);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream) {
-  switch (D) {
-    case 64: return launch_fwd_d<64>(args, stream);
-    case 96: return launch_fwd_d<96>(args, stream);
-    case 128: return launch_fwd_d<128>(args, stream);
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_fwd_ord_bf16(const FwdArgs& args, int D, hipStream_t stream) {
+  return launch_fwd_which(args, D, stream, 0);
+}
+hipError_t launch_fwd_frz_bf16(const FwdArgs& args, int D, hipStream_t stream) {
+  return launch_fwd_which(args, D, stream, 1);
 }
 
 }  // namespace saf

@@ -2,14 +2,16 @@
 // ("When Can Attention Heads Be Statically Defined?", Section 3.2,
 // Equation 3: N(i) = sum_{k<=i} exp(a[k] + r[i-k])).
 //
-// Normaliser kernel.  One thread per row i, 256 rows per block, keys in
-// tiles of 256.  Within a (row block, key tile) the terms factor as
+// Normaliser kernel.  One block per (head, 64-row block); each of its four
+// waves takes every fourth key of a row, so a row's sum is split over four
+// lanes and merged at the end.  Keys come in tiles of 256.  Within a
+// (row block, key tile) the terms factor as
 //   exp2(a2[k] + r2[i-k]) = 2^(ma + mr) * exp2(a2[k] - ma) * exp2(r2[i-k] - mr)
 // with ma, mr the tile maxima of a2 and of the tile's r2 band (log2 units),
 // so each term costs one FMA on two staged exponentials.  Both factors are
-// <= 1; a term lost to underflow is below 2^-126 of 2^(ma+mr), so when the
-// tile sum is >= 2^-20 the relative loss is below 2^-98.  Tiles whose sum is
-// smaller are recomputed exactly with a max-shifted sum.  Tile results are
+// <= 1; a term lost to underflow is below 2^-126 of 2^(ma+mr), so when a
+// lane's tile sum is >= 2^-20 the relative loss is below 2^-98.  Smaller
+// sums are recomputed exactly with a max-shifted sum.  Partial results are
 // merged with a running (max, sum) log-sum-exp.
 #include "saf_internal.h"
 #include "saf_device.h"
@@ -17,7 +19,8 @@
 namespace saf {
 namespace {
 
-constexpr int kRows = 256;  // rows per block (one per thread)
+constexpr int kRows = 64;   // rows per block (one per lane of each wave)
+constexpr int kLanes = 4;   // key lanes: wave w takes keys w, w+4, w+8, ...
 constexpr int kTK = 256;    // keys per tile
 constexpr int kBand = kRows + kTK;
 
@@ -31,34 +34,38 @@ __device__ __forceinline__ float block_max(float v, float* red) {
   return m;
 }
 
-__global__ __launch_bounds__(kRows) void lognorm_kernel(LognormArgs A, int identity_heads) {
+__global__ __launch_bounds__(kRows * kLanes) void lognorm_kernel(LognormArgs A, int identity_heads) {
   __shared__ float a2s[kTK];    // a (log2 units) of the tile
   __shared__ float r2s[kBand];  // r (log2 units) of the tile's band
   __shared__ float eas[kTK];    // exp2(a2 - ma)
   __shared__ float ers[kBand];  // exp2(r2 - mr)
   __shared__ float red[8];
+  __shared__ float cm_s[kLanes][kRows];
+  __shared__ float cs_s[kLanes][kRows];
 
   const int hidx = blockIdx.y;
   const int h = identity_heads ? hidx : (int)A.heads[hidx];
   const int T = A.T;
   const int i0 = blockIdx.x * kRows;
-  const int i = i0 + threadIdx.x;
+  const int row = lane_id(), kl = wave_id();
+  const int i = i0 + row;
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
   const int last_row = min(i0 + kRows, T) - 1;
+  constexpr int NT = kRows * kLanes;
 
-  float M = kNegInf, S = 0.f;  // running log2-sum-exp of this row
+  float M = kNegInf, S = 0.f;  // running log2-sum-exp of this lane's share of the row
   for (int k0 = 0; k0 <= last_row; k0 += kTK) {
     // stage a2 over the tile keys and r2 over offsets [i0-k0-kTK+1, i0+kRows-1-k0]
     const int dmin = i0 - k0 - (kTK - 1);
     float lmax_a = kNegInf, lmax_r = kNegInf;
-    for (int x = threadIdx.x; x < kTK; x += kRows) {
+    for (int x = threadIdx.x; x < kTK; x += NT) {
       const int k = k0 + x;
       const float v = (k < T) ? arow[k] * kLog2e : kNegInf;
       a2s[x] = v;
       lmax_a = fmaxf(lmax_a, v);
     }
-    for (int x = threadIdx.x; x < kBand; x += kRows) {
+    for (int x = threadIdx.x; x < kBand; x += NT) {
       const int d = dmin + x;
       const float v = (d >= 0 && d < T) ? rrow[d] * kLog2e : kNegInf;
       r2s[x] = v;
@@ -69,26 +76,26 @@ __global__ __launch_bounds__(kRows) void lognorm_kernel(LognormArgs A, int ident
     float mr = block_max(lmax_r, red + 4);
     if (ma == kNegInf) ma = 0.f;
     if (mr == kNegInf) mr = 0.f;
-    for (int x = threadIdx.x; x < kTK; x += kRows) eas[x] = fast_exp2(a2s[x] - ma);
-    for (int x = threadIdx.x; x < kBand; x += kRows) ers[x] = fast_exp2(r2s[x] - mr);
+    for (int x = threadIdx.x; x < kTK; x += NT) eas[x] = fast_exp2(a2s[x] - ma);
+    for (int x = threadIdx.x; x < kBand; x += NT) ers[x] = fast_exp2(r2s[x] - mr);
     __syncthreads();
 
-    if (i < T && k0 <= i) {
+    if (i < T && k0 + kl <= i) {
       const int kend = min(kTK - 1, i - k0);  // last tile-local key of this row
       const int xb = i - k0 - dmin;           // band index of offset i - k0
       float s = 0.f;
-      for (int x = 0; x <= kend; ++x) s = fmaf(eas[x], ers[xb - x], s);
+      for (int x = kl; x <= kend; x += kLanes) s = fmaf(eas[x], ers[xb - x], s);
       float cm, cs;
       if (s >= 0x1p-20f) {
         cm = ma + mr;
         cs = s;
       } else {
-        // exact fallback: max-shifted sum of this row's terms in the tile
+        // exact fallback: max-shifted sum of this lane's terms in the tile
         cm = kNegInf;
-        for (int x = 0; x <= kend; ++x) cm = fmaxf(cm, a2s[x] + r2s[xb - x]);
+        for (int x = kl; x <= kend; x += kLanes) cm = fmaxf(cm, a2s[x] + r2s[xb - x]);
         cs = 0.f;
         if (cm != kNegInf)
-          for (int x = 0; x <= kend; ++x) cs += fast_exp2(a2s[x] + r2s[xb - x] - cm);
+          for (int x = kl; x <= kend; x += kLanes) cs += fast_exp2(a2s[x] + r2s[xb - x] - cm);
       }
       if (cs > 0.f) {
         const float Mn = fmaxf(M, cm);
@@ -98,9 +105,19 @@ __global__ __launch_bounds__(kRows) void lognorm_kernel(LognormArgs A, int ident
     }
     __syncthreads();
   }
-  if (i < T) {
-    const float lz = (M + fast_log2(S)) * kLn2;  // natural log
-    for (int b = 0; b < A.B; ++b) A.out[(int64_t)b * A.out_b_stride + (int64_t)h * A.out_h_stride + i] = lz;
+  cm_s[kl][row] = M;
+  cs_s[kl][row] = S;
+  __syncthreads();
+  if (kl == 0 && i < T) {
+    float Mt = kNegInf;
+    for (int x = 0; x < kLanes; ++x)
+      if (cs_s[x][row] > 0.f) Mt = fmaxf(Mt, cm_s[x][row]);
+    float St = 0.f;
+    for (int x = 0; x < kLanes; ++x)
+      if (cs_s[x][row] > 0.f) St += cs_s[x][row] * fast_exp2(cm_s[x][row] - Mt);
+    const float lz = (Mt + fast_log2(St)) * kLn2;  // natural log
+    for (int b = 0; b < A.B; ++b)
+      A.out[(int64_t)b * A.out_b_stride + (int64_t)h * A.out_h_stride + i] = lz;
   }
 }
 
@@ -133,14 +150,14 @@ __global__ __launch_bounds__(256) void pattern_dense_kernel(int T, const float* 
 hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream) {
   if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
   dim3 grid((args.T + kRows - 1) / kRows, args.n_heads);
-  hipLaunchKernelGGL(lognorm_kernel, grid, dim3(kRows), 0, stream, args, 0);
+  hipLaunchKernelGGL(lognorm_kernel, grid, dim3(kRows * kLanes), 0, stream, args, 0);
   return hipGetLastError();
 }
 
 hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream) {
   if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
   dim3 grid((args.T + kRows - 1) / kRows, args.n_heads);
-  hipLaunchKernelGGL(lognorm_kernel, grid, dim3(kRows), 0, stream, args, 1);
+  hipLaunchKernelGGL(lognorm_kernel, grid, dim3(kRows * kLanes), 0, stream, args, 1);
   return hipGetLastError();
 }
 

@@ -32,6 +32,18 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+// LDS pointers carry their address space so that every access compiles to a
+// ds_* instruction (a generic pointer would become a flat access).
+typedef __attribute__((address_space(3))) __bf16 lds_bf16;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+// Base of the dynamic LDS allocation as an LDS pointer.
+#define SAF_DYN_LDS(name)                                   \
+  extern __shared__ __align__(16) char name##_raw[];         \
+  lds_bf16* name = (lds_bf16*)(name##_raw)
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -63,15 +75,14 @@ __device__ __forceinline__ bf16x8 pack_acc8(const f32x16& c, int r0) {
 }
 
 // 16-byte LDS read: 8 consecutive bf16 at element offset `off` of `base`.
-__device__ __forceinline__ bf16x8 lds_read8(const __bf16* base, int off) {
-  return *reinterpret_cast<const bf16x8*>(base + off);
+__device__ __forceinline__ bf16x8 lds_read8(const lds_bf16* base, int off) {
+  return *(const lds_bf16x8*)(base + off);
 }
 
 // Transposed 4-element read (see header comment); `off` is the element
 // offset this lane addresses.
-__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* base, int off) {
-  const lds_char* p = (const lds_char*)(base) + 2 * off;
-  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+__device__ __forceinline__ bf16x4 lds_read_tr4(const lds_bf16* base, int off) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off));
   return __builtin_bit_cast(bf16x4, t);
 }
 
@@ -89,7 +100,7 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 // i.e. slot e of half h maps to row row0 + 8*(e/4) + 4*h + e%4 -- exactly the
 // row labelling of the C registers 8*(s%2)..8*(s%2)+7 of a 32x32 accumulator
 // block, so a C block converted with pack_acc8 pairs with this operand.
-__device__ __forceinline__ bf16x8 lds_frag_tr(const __bf16* X, int pitch, int row0, int col0) {
+__device__ __forceinline__ bf16x8 lds_frag_tr(const lds_bf16* X, int pitch, int row0, int col0) {
   const int l = lane_id();
   const int g = l >> 4;        // 16-lane group
   const int s16 = l & 15;
@@ -103,7 +114,7 @@ __device__ __forceinline__ bf16x8 lds_frag_tr(const __bf16* X, int pitch, int ro
 
 // MFMA operand whose k index runs along columns of a row-major LDS tile:
 // lane l receives X[row0 + l%32][col0 + 8*(l/32) + e], e = 0..7.
-__device__ __forceinline__ bf16x8 lds_frag_nat(const __bf16* X, int pitch, int row0, int col0) {
+__device__ __forceinline__ bf16x8 lds_frag_nat(const lds_bf16* X, int pitch, int row0, int col0) {
   const int l = lane_id();
   return lds_read8(X, (row0 + (l & 31)) * pitch + col0 + 8 * (l >> 5));
 }
@@ -116,5 +127,7 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void sstore16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void lds_store16(lds_bf16* p, u32x4 v) { *(lds_u32x4*)p = v; }
+__device__ __forceinline__ f32x4 lds_read_f4(const lds_f32* p) { return *(const lds_f32x4*)p; }
 
 }  // namespace saf

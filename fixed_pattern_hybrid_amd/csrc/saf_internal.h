@@ -69,11 +69,17 @@ hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream);
 hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const float* r, float* w,
                                 hipStream_t stream);
 
-hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
+
+// bf16 path: ordinary and frozen heads run as separate kernels.
+hipError_t launch_fwd_ord_bf16(const FwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_fwd_frz_bf16(const FwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream);
-hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_ord_bf16(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_frz_bf16(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream);
 
+// fp32 path: one kernel per pass covers both head kinds.
 hipError_t launch_fwd_f32(const FwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_pre_f32(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_kv_f32(const BwdArgs& args, int D, hipStream_t stream);

@@ -30,12 +30,12 @@ struct TileStage {
     }
   }
 
-  __device__ __forceinline__ void store(__bf16* lds, int pitch) const {
+  __device__ __forceinline__ void store(lds_bf16* lds, int pitch) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = threadIdx.x + p * NTHR;
       const int row = idx / CPR, ch = idx % CPR;
-      sstore16(lds + row * pitch + ch * 8, buf[p]);
+      lds_store16(lds + row * pitch + ch * 8, buf[p]);
     }
   }
 };

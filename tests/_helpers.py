@@ -31,6 +31,28 @@ def max_abs(got, ref) -> float:
     return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))))
 
 
+def bf16_half_ulp(x) -> np.ndarray:
+    """Half a unit in the last place of bfloat16 at |x| (8-bit significand)."""
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
+    return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def out_max_abs(got, ref, dtype: str) -> float:
+    """Forward max-abs error of an output stored as ``dtype``.
+
+    For bf16 outputs the half-ulp of the stored value is subtracted first: an
+    exact result rounded to bf16 already differs from the float64 value by up
+    to that much (0.0156 for |O| in [4, 8)), so the bar applies to the error
+    beyond the storage format's own rounding.  fp32: plain max-abs.
+    """
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    if dtype == "bf16":
+        err = err - bf16_half_ulp(np.maximum(np.abs(got), np.abs(ref)))
+    return float(max(np.max(err), 0.0))
+
+
 def torch_dtype(cfg):
     return torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
 
