@@ -33,6 +33,9 @@ COMMON_FLAGS = [
     "-Wno-unused-function",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax/rescale VALU work touches them
+    # every tile, and AGPR accumulators would need a copy each way
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -18,6 +18,8 @@
 //             lane owns one key and the C registers of S feed the products.
 //   bwd_q   : one program per (b, h, 128-query block) of ordinary heads;
 //             keys in tiles of 64; accumulator dQ^T.
+#include <type_traits>
+
 #include "saf_internal.h"
 #include "saf_tile.h"
 
@@ -32,16 +34,18 @@ constexpr int kQBN = 64;         // keys per tile in the query-block pass
 
 template <int D>
 struct BwdCfg {
-  static constexpr int PITCH = D + 8;
+  static constexpr int PITCH = LdsLayout<D>::PITCH;
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
-  static constexpr int G = (D <= 64) ? 4 : 2;
+  static constexpr int G = 2;
   static constexpr int TILE = 64 * PITCH;
   static constexpr int BAND = kKvBM + kKvBN;  // r band of a (query tile, key block)
+  // per buffer: z2[kKvBM], then 4 copies of the band, copy c shifted by c
+  static constexpr int FSTRIDE = kKvBM + 4 * BAND;
   // key-block pass, ordinary: Q and dO tiles (double-buffered) + lse2 and delta
   static constexpr size_t kv_ord_lds = size_t(2) * 2 * TILE * 2 + size_t(2) * 2 * kKvBM * 4;
   // key-block pass, frozen: G dO tiles (double-buffered) + z2 and the r band
-  static constexpr size_t kv_frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * (kKvBM + BAND) * 4;
+  static constexpr size_t kv_frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4;
   static constexpr size_t kv_lds = kv_ord_lds > kv_frz_lds ? kv_ord_lds : kv_frz_lds;
   static constexpr size_t q_lds = size_t(2) * 2 * TILE * 2;
 };
@@ -108,7 +112,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
 // Key-block pass, ordinary head (b, h, kb).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void bwd_kv_ord_kernel(BwdArgs A) {
   using C = BwdCfg<D>;
   SAF_DYN_LDS(smem);
   const int per_k = A.B * A.n_ord;
@@ -163,8 +167,8 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
   if (qt0 < nqt) {
     qst.load(qg, A.q.st, qt0 * kKvBM, T);
     ost.load(dog, A.dout.st, qt0 * kKvBM, T);
-    qst.store(smem, C::PITCH);
-    ost.store(smem + 2 * C::TILE, C::PITCH);
+    qst.store(smem);
+    ost.store(smem + 2 * C::TILE);
     stage_vec(qt0 * kKvBM, 0);
   }
   __syncthreads();
@@ -177,7 +181,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
   }
   const float sl2 = A.scale_log2;
 
-  for (int qt = qt0; qt < nqt; ++qt) {
+  // One query tile.  MASK only for the two tiles that overlap the key
+  // block's diagonal (queries k0 .. k0+127); later tiles need no mask.
+  auto tile = [&](int qt, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
@@ -189,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
     const lds_bf16* O = smem + (2 + bi) * C::TILE;
     const lds_f32* ls = fb + bi * kKvBM;
     const lds_f32* ds = fb + (2 + bi) * kKvBM;
-    if (i0 + kKvBM - 1 >= wk_lo) {
+    if (!MASK || i0 + kKvBM - 1 >= wk_lo) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -197,11 +204,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
         dp[c] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          s[c] = mfma32(lds_frag_nat(Q, C::PITCH, 32 * c, 16 * ks), kf[ks], s[c]);
-          dp[c] = mfma32(lds_frag_nat(O, C::PITCH, 32 * c, 16 * ks), vf[ks], dp[c]);
+          s[c] = mfma32(lds_frag_nat<D>(Q, 32 * c, 16 * ks), kf[ks], s[c]);
+          dp[c] = mfma32(lds_frag_nat<D>(O, 32 * c, 16 * ks), vf[ks], dp[c]);
         }
       }
-      const bool diag = i0 < wk_lo + 31;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -213,7 +219,9 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
             float p = fast_exp2(fmaf(s[c][r], sl2, -l4[e]));
-            if (diag && (i0 + ib + e) < j) p = 0.f;
+            if constexpr (MASK) {
+              if ((i0 + ib + e) < j) p = 0.f;
+            }
             s[c][r] = p;
             dp[c][r] = p * (dp[c][r] - d4[e]);
           }
@@ -225,18 +233,22 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_ord_kernel(BwdArgs A) {
         const bf16x8 sf = pack_acc8(dp[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          dva[db] = mfma32(lds_frag_tr(O, C::PITCH, 16 * st, 32 * db), pf, dva[db]);
-          dka[db] = mfma32(lds_frag_tr(Q, C::PITCH, 16 * st, 32 * db), sf, dka[db]);
+          dva[db] = mfma32(lds_frag_tr<D>(O, 16 * st, 32 * db), pf, dva[db]);
+          dka[db] = mfma32(lds_frag_tr<D>(Q, 16 * st, 32 * db), sf, dka[db]);
         }
       }
     }
     if (more) {
-      qst.store(smem + (bi ^ 1) * C::TILE, C::PITCH);
-      ost.store(smem + (2 + (bi ^ 1)) * C::TILE, C::PITCH);
+      qst.store(smem + (bi ^ 1) * C::TILE);
+      ost.store(smem + (2 + (bi ^ 1)) * C::TILE);
       stage_vec(i0 + kKvBM, bi ^ 1);
     }
     __syncthreads();
-  }
+  };
+  const int qt_full = min(qt0 + 2, nqt);
+  int qt = qt0;
+  for (; qt < qt_full; ++qt) tile(qt, std::true_type{});
+  for (; qt < nqt; ++qt) tile(qt, std::false_type{});
   store_rows_t<D>(A.dv, b, h, j, T, dva, 1.f);
   store_rows_t<D>(A.dk, b, h, j, T, dka, A.scale);
 }
@@ -267,9 +279,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
   const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
   const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, same for every b
 
-  // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and the r band[BAND]
+  // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and 4 shifted copies
+  // of the r band (copy c holds band[y + c] at y)
   lds_f32* fb = (lds_f32*)(smem + 2 * G * C::TILE);
-  constexpr int FSTRIDE = kKvBM + C::BAND;
+  constexpr int FSTRIDE = C::FSTRIDE;
 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
   };
   auto store_do = [&](int buf) {
 #pragma unroll
-    for (int gb = 0; gb < G; ++gb) ost[gb].store(smem + (buf * G + gb) * C::TILE, C::PITCH);
+    for (int gb = 0; gb < G; ++gb) ost[gb].store(smem + (buf * G + gb) * C::TILE);
   };
   // z2 = log N (log2 units) of the tile rows; r band over offsets
   // [i0 - k0 - (BN-1), i0 + BM - 1 - k0].
@@ -297,9 +310,10 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
       zs[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();
     }
     const int dmin = i0 - k0 - (kKvBN - 1);
-    for (int x = threadIdx.x; x < C::BAND; x += kThreads) {
-      const int d = dmin + x;
-      rs[x] = (d >= 0 && d < T) ? rrow[d] * kLog2e : kNegInf;
+    for (int x = threadIdx.x; x < 4 * C::BAND; x += kThreads) {
+      const int c = x / C::BAND, y = x - c * C::BAND;
+      const int d = dmin + y + c;
+      rs[x] = (y + c < C::BAND && d >= 0 && d < T) ? rrow[d] * kLog2e : kNegInf;
     }
   };
 
@@ -324,22 +338,29 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
     const lds_f32* zs = fb + bi * FSTRIDE;
     const lds_f32* rs = zs + kKvBM;
     if (i0 + kKvBM - 1 >= wk_lo) {
-      // band index of (i, j): (i - i0) - (j - k0) + BN - 1
+      // band index of (i, j): (i - i0) - (j - k0) + BN - 1.  Four consecutive
+      // rows base..base+3 (base a multiple of 4) read band[base + xj + 0..3],
+      // and (base + xj) mod 4 = xj mod 4 is fixed per lane.
       const int xj = (kKvBN - 1) - (j - k0);
+      const int cpy = xj & 3;
+      const lds_f32* rc = rs + cpy * C::BAND - cpy;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int ii = 16 * st + 8 * (e >> 2) + 4 * hl + (e & 3);  // tile row
-          wv[e] = fast_exp2(a2 + rs[ii + xj] - zs[ii]);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int base = 16 * st + 8 * hh + 4 * hl;  // first of four tile rows
+          const f32x4 z4 = lds_read_f4(zs + base);
+          const f32x4 r4 = lds_read_f4(rc + base + xj);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wv[4 * hh + k] = fast_exp2(a2 + r4[k] - z4[k]);
         }
         const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
 #pragma unroll
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            dva[gb][db] = mfma32(lds_frag_tr(smem + (bi * G + gb) * C::TILE, C::PITCH, 16 * st, 32 * db),
+            dva[gb][db] = mfma32(lds_frag_tr<D>(smem + (bi * G + gb) * C::TILE, 16 * st, 32 * db),
                                  wf, dva[gb][db]);
       }
     }
@@ -400,8 +421,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   TileStage<D, kQBN, kThreads> kst, vst;
   kst.load(kg, A.k.st, 0, T);
   vst.load(vg, A.v.st, 0, T);
-  kst.store(smem, C::PITCH);
-  vst.store(smem + 2 * C::TILE, C::PITCH);
+  kst.store(smem);
+  vst.store(smem + 2 * C::TILE);
   __syncthreads();
 
   f32x16 dqa[C::NDB];
@@ -409,7 +430,9 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   for (int db = 0; db < C::NDB; ++db) dqa[db] = f32x16{};
   const float sl2 = A.scale_log2;
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile.  MASK only for the tiles that reach the diagonal.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int j0 = t * kQBN;
     const bool more = (t + 1) < ntiles;
     if (more) {
@@ -418,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
     }
     const lds_bf16* K = smem + (t & 1) * C::TILE;
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
-    if (j0 <= wq_hi) {
+    if (!MASK || j0 <= wq_hi) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
@@ -426,17 +449,16 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
         dp[c] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
-          s[c] = mfma32(lds_frag_nat(K, C::PITCH, 32 * c, 16 * ks), qf[ks], s[c]);
-          dp[c] = mfma32(lds_frag_nat(V, C::PITCH, 32 * c, 16 * ks), of[ks], dp[c]);
+          s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
+          dp[c] = mfma32(lds_frag_nat<D>(V, 32 * c, 16 * ks), of[ks], dp[c]);
         }
       }
-      const bool diag = j0 + kQBN - 1 > wq_lo;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float p = fast_exp2(fmaf(s[c][r], sl2, -l2));
-          if (diag) {
+          if constexpr (MASK) {
             const int jj = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
             if (jj > i) p = 0.f;
           }
@@ -448,15 +470,19 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
         const bf16x8 sf = pack_acc8(dp[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-          dqa[db] = mfma32(lds_frag_tr(K, C::PITCH, 16 * st, 32 * db), sf, dqa[db]);
+          dqa[db] = mfma32(lds_frag_tr<D>(K, 16 * st, 32 * db), sf, dqa[db]);
       }
     }
     if (more) {
-      kst.store(smem + ((t + 1) & 1) * C::TILE, C::PITCH);
-      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE, C::PITCH);
+      kst.store(smem + ((t + 1) & 1) * C::TILE);
+      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE);
     }
     __syncthreads();
-  }
+  };
+  const int t_diag = min(q0 / kQBN, ntiles);
+  int t = 0;
+  for (; t < t_diag; ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
   store_rows_t<D>(A.dq, b, h, i, T, dqa, A.scale);
 }
 

@@ -20,6 +20,8 @@
 // one query: row max, row sum and rescaling stay in the lane, and the C
 // registers of S^T convert directly into the B operand of the second product
 // (V^T comes from LDS through transposing reads).
+#include <type_traits>
+
 #include "saf_internal.h"
 #include "saf_tile.h"
 
@@ -32,14 +34,16 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct FwdCfg {
-  static constexpr int PITCH = D + 8;  // LDS row pitch (elements)
+  static constexpr int PITCH = LdsLayout<D>::PITCH;  // LDS row pitch (elements)
   static constexpr int NDB = D / 32;   // 32-wide blocks of the head dimension
   static constexpr int NKS = D / 16;   // 16-deep k steps over the head dimension
-  static constexpr int G = (D <= 64) ? 4 : 2;  // batch elements per frozen program
+  static constexpr int G = 2;                  // batch elements per frozen program
   static constexpr int TILE = kBN * PITCH;     // elements of one staged tile
   static constexpr int BAND = kBM + kBN;       // r band length (BM + BN - 1, padded)
+  // per buffer: a2[kBN], then 4 copies of the band, copy c shifted by c
+  static constexpr int FSTRIDE = kBN + 4 * BAND;
   static constexpr size_t ord_lds = size_t(2) * 2 * TILE * 2;
-  static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * (kBN + BAND) * 4;
+  static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4;
 };
 
 template <int D>
@@ -106,8 +110,8 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
   TileStage<D, kBN, kThreads> kst, vst;
   kst.load(kg, A.k.st, 0, T);
   vst.load(vg, A.v.st, 0, T);
-  kst.store(smem, C::PITCH);
-  vst.store(smem + 2 * C::TILE, C::PITCH);
+  kst.store(smem);
+  vst.store(smem + 2 * C::TILE);
   __syncthreads();
 
   f32x16 oacc[C::NDB];
@@ -116,7 +120,11 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
   float m_run = kNegInf, l_run = 0.f;
   const float sl2 = A.scale_log2;
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One key tile: S^T = K Q^T, online softmax, O^T += V^T P^T.  MASK is set
+  // only for the tiles that reach the diagonal (the last two of the block),
+  // so the unmasked tiles carry no masking instructions.
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
     if (more) {
@@ -125,17 +133,16 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
     }
     const lds_bf16* K = smem + (t & 1) * C::TILE;
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
-    if (j0 <= wq_hi) {
+    if (!MASK || j0 <= wq_hi) {
       f32x16 s[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         s[c] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks)
-          s[c] = mfma32(lds_frag_nat(K, C::PITCH, 32 * c, 16 * ks), qf[ks], s[c]);
+          s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
       }
-      // causal mask where the tile reaches past this wave's first query
-      if (j0 + kBN - 1 > wq_lo) {
+      if constexpr (MASK) {
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -150,7 +157,13 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
       mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * sl2);
+      // Lazy rescaling: the reference maximum only moves when the tile's
+      // maximum exceeds it by more than 8 (log2 units), so p <= 2^8 and the
+      // accumulator rescale is skipped on most tiles.  The final O = acc / l
+      // and lse = m + log2(l) are exact for any reference value.
+      const float mt = mx * sl2;
+      const bool grow = mt > m_run + 8.f;
+      const float m_new = grow ? mt : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       float psum = 0.f;
 #pragma unroll
@@ -163,7 +176,9 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
         }
       l_run = fmaf(l_run, alpha, psum);
       m_run = m_new;
-      if (__any(alpha != 1.f)) {
+      if (__any(grow)) {
+        // keep this a real branch (it is taken on few tiles)
+        asm volatile("");
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -175,15 +190,21 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
         const bf16x8 pf = pack_acc8(s[st >> 1], 8 * (st & 1));
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db)
-          oacc[db] = mfma32(lds_frag_tr(V, C::PITCH, 16 * st, 32 * db), pf, oacc[db]);
+          oacc[db] = mfma32(lds_frag_tr<D>(V, 16 * st, 32 * db), pf, oacc[db]);
       }
     }
     if (more) {
-      kst.store(smem + ((t + 1) & 1) * C::TILE, C::PITCH);
-      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE, C::PITCH);
+      kst.store(smem + ((t + 1) & 1) * C::TILE);
+      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE);
     }
     __syncthreads();
-  }
+  };
+
+  // tiles with every key below the block's first query need no mask
+  const int t_diag = min(q0 / kBN, ntiles);
+  int t = 0;
+  for (; t < t_diag; ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
 
   const float l_tot = l_run + xor32(l_run);
   store_out_rows<D>(A.o, b, h, i, T, oacc, 1.f / l_tot);
@@ -214,9 +235,11 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
   const int b0 = grp * G;
   const int nb = min(G, A.B - b0);
 
-  // LDS: V tiles [buf][gb], then per buffer a2[kBN] and the r band[BAND]
+  // LDS: V tiles [buf][gb], then per buffer a2[kBN] and 4 shifted copies of
+  // the r band (copy c holds band[y + c] at y), so that each lane reads the
+  // four offsets of four consecutive keys with one aligned 16-byte read.
   lds_f32* fbase = (lds_f32*)(smem + 2 * G * C::TILE);
-  constexpr int FSTRIDE = kBN + C::BAND;
+  constexpr int FSTRIDE = C::FSTRIDE;
 
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
@@ -225,7 +248,8 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
-  // a (log2 units) for the tile keys and r over offsets of the tile's band.
+  // a (log2 units) for the tile keys; band[x] = r2[dmin + x] for the offsets
+  // of the tile, -inf outside [0, T), in four shifted copies.
   auto stage_pattern = [&](int j0, lds_f32* as) {
     lds_f32* rs = as + kBN;
     for (int x = threadIdx.x; x < kBN; x += kThreads) {
@@ -233,9 +257,10 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
       as[x] = (j < T) ? arow[j] * kLog2e : kNegInf;
     }
     const int dmin = q0 - j0 - (kBN - 1);
-    for (int x = threadIdx.x; x < C::BAND; x += kThreads) {
-      const int dl = dmin + x;
-      rs[x] = (dl >= 0 && dl < T) ? rrow[dl] * kLog2e : kNegInf;
+    for (int x = threadIdx.x; x < 4 * C::BAND; x += kThreads) {
+      const int c = x / C::BAND, y = x - c * C::BAND;
+      const int dl = dmin + y + c;
+      rs[x] = (y + c < C::BAND && dl >= 0 && dl < T) ? rrow[dl] * kLog2e : kNegInf;
     }
   };
 
@@ -250,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
   };
   auto store_v = [&](int buf) {
 #pragma unroll
-    for (int gb = 0; gb < G; ++gb) vst[gb].store(smem + (buf * G + gb) * C::TILE, C::PITCH);
+    for (int gb = 0; gb < G; ++gb) vst[gb].store(smem + (buf * G + gb) * C::TILE);
   };
 
   load_v(0);
@@ -272,22 +297,29 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
     const lds_f32* as = fbase + buf * FSTRIDE;
     const lds_f32* rs = as + kBN;
     if (j0 <= wq_hi) {
-      // band index of (i, j): (i - q0) - (j - j0) + BN - 1
+      // band index of (i, j): (i - q0) - (j - j0) + BN - 1.  For four keys
+      // base..base+3 (base a multiple of 4) the offsets are y0+3..y0 with
+      // y0 = xi - base - 3, and y0 mod 4 = (xi + 1) mod 4 is fixed per lane.
       const int xi = (i - q0) + kBN - 1;
+      const int cpy = (xi + 1) & 3;
+      const lds_f32* rc = rs + cpy * C::BAND - cpy;  // rc[y] = band[y] for y = 0 mod 4 reads
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int jj = 16 * st + 8 * (e >> 2) + 4 * hl + (e & 3);
-          wv[e] = fast_exp2(as[jj] + rs[xi - jj] - z2);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int base = 16 * st + 8 * hh + 4 * hl;
+          const f32x4 a4 = lds_read_f4(as + base);
+          const f32x4 r4 = lds_read_f4(rc + (xi - base - 3));  // band[y0 .. y0+3]
+#pragma unroll
+          for (int k = 0; k < 4; ++k) wv[4 * hh + k] = fast_exp2(a4[k] + r4[3 - k] - z2);
         }
         const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
 #pragma unroll
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            oacc[gb][db] = mfma32(lds_frag_tr(smem + (buf * G + gb) * C::TILE, C::PITCH, 16 * st, 32 * db),
+            oacc[gb][db] = mfma32(lds_frag_tr<D>(smem + (buf * G + gb) * C::TILE, 16 * st, 32 * db),
                                   wf, oacc[gb][db]);
       }
     }

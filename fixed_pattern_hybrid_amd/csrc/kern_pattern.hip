@@ -21,8 +21,24 @@ namespace {
 
 constexpr int kRows = 64;   // rows per block (one per lane of each wave)
 constexpr int kLanes = 4;   // key lanes: wave w takes keys w, w+4, w+8, ...
-constexpr int kTK = 256;    // keys per tile
+constexpr int kTK = 1024;   // keys per tile
 constexpr int kBand = kRows + kTK;
+
+// Maxima of two values over the block (4 waves); red holds 8 floats.
+__device__ __forceinline__ void block_max2(float& u, float& v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    u = fmaxf(u, __shfl_xor(u, o, 64));
+    v = fmaxf(v, __shfl_xor(v, o, 64));
+  }
+  __syncthreads();
+  if (lane_id() == 0) {
+    red[wave_id()] = u;
+    red[4 + wave_id()] = v;
+  }
+  __syncthreads();
+  u = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  v = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+}
 
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -72,8 +88,8 @@ __global__ __launch_bounds__(kRows * kLanes) void lognorm_kernel(LognormArgs A, 
       lmax_r = fmaxf(lmax_r, v);
     }
     // shifts; an all -inf tile (possible only for -inf inputs) shifts by 0
-    float ma = block_max(lmax_a, red);
-    float mr = block_max(lmax_r, red + 4);
+    float ma = lmax_a, mr = lmax_r;
+    block_max2(ma, mr, red);
     if (ma == kNegInf) ma = 0.f;
     if (mr == kNegInf) mr = 0.f;
     for (int x = threadIdx.x; x < kTK; x += NT) eas[x] = fast_exp2(a2s[x] - ma);
@@ -83,8 +99,16 @@ __global__ __launch_bounds__(kRows * kLanes) void lognorm_kernel(LognormArgs A, 
     if (i < T && k0 + kl <= i) {
       const int kend = min(kTK - 1, i - k0);  // last tile-local key of this row
       const int xb = i - k0 - dmin;           // band index of offset i - k0
-      float s = 0.f;
-      for (int x = kl; x <= kend; x += kLanes) s = fmaf(eas[x], ers[xb - x], s);
+      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+      int x = kl;
+      for (; x + 3 * kLanes <= kend; x += 4 * kLanes) {
+        s0 = fmaf(eas[x], ers[xb - x], s0);
+        s1 = fmaf(eas[x + kLanes], ers[xb - x - kLanes], s1);
+        s2 = fmaf(eas[x + 2 * kLanes], ers[xb - x - 2 * kLanes], s2);
+        s3 = fmaf(eas[x + 3 * kLanes], ers[xb - x - 3 * kLanes], s3);
+      }
+      for (; x <= kend; x += kLanes) s0 = fmaf(eas[x], ers[xb - x], s0);
+      const float s = (s0 + s1) + (s2 + s3);
       float cm, cs;
       if (s >= 0x1p-20f) {
         cm = ma + mr;

@@ -93,30 +93,60 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
   return v;
 }
 
-// MFMA operand whose k index runs along rows of a row-major LDS tile X with
-// row pitch `pitch` (elements).  Lane l receives
+// Row-major [rows][D] bf16 tile in LDS.  For D = 64 and 128 rows are unpadded
+// and their 16-byte chunks are XOR-swizzled by row, chunk' = chunk ^ swz(row):
+//   swz = ((row & 3) << 1) | ((row >> 2) & 1)        (8 chunks, D = 64)
+//       | ((row >> 3) & 1) << 3                      (16 chunks, D = 128)
+// so that 8 (or 16) consecutive rows read at one column hit distinct chunks
+// (natural 16-byte fragment reads), and 4 consecutive rows read over an
+// aligned group of 4 chunks (transpose reads) hit 4 disjoint chunk groups.
+// Other D use a padded pitch of D + 8 without swizzle.
+template <int D>
+struct LdsLayout {
+  static constexpr bool SWZ = (D == 64 || D == 128);
+  static constexpr int PITCH = SWZ ? D : D + 8;  // elements per row
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (!SWZ) {
+      return 0;
+    } else {
+      int f = ((row & 3) << 1) | ((row >> 2) & 1);
+      if constexpr (D >= 128) f |= ((row >> 3) & 1) << 3;
+      return f;
+    }
+  }
+  // element offset of (row, col); col is a multiple of 4
+  __device__ static __forceinline__ int off(int row, int col) {
+    return row * PITCH + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+  }
+};
+
+// MFMA operand whose k index runs along rows of a row-major LDS tile X.
+// Lane l receives
 //   X[row0 + 4*(l/32) + e][col0 + l%32]       for e = 0..3 (slots 0..3)
 //   X[row0 + 8 + 4*(l/32) + e][col0 + l%32]   for e = 0..3 (slots 4..7)
 // i.e. slot e of half h maps to row row0 + 8*(e/4) + 4*h + e%4 -- exactly the
 // row labelling of the C registers 8*(s%2)..8*(s%2)+7 of a 32x32 accumulator
 // block, so a C block converted with pack_acc8 pairs with this operand.
-__device__ __forceinline__ bf16x8 lds_frag_tr(const lds_bf16* X, int pitch, int row0, int col0) {
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag_tr(const lds_bf16* X, int row0, int col0) {
+  using L = LdsLayout<D>;
   const int l = lane_id();
   const int g = l >> 4;        // 16-lane group
   const int s16 = l & 15;
   const int e = s16 >> 2, c = s16 & 3;
   const int row = row0 + 4 * (g >> 1) + e;
   const int col = col0 + 16 * (g & 1) + 4 * c;
-  bf16x4 lo = lds_read_tr4(X, row * pitch + col);
-  bf16x4 hi = lds_read_tr4(X, (row + 8) * pitch + col);
+  bf16x4 lo = lds_read_tr4(X, L::off(row, col));
+  bf16x4 hi = lds_read_tr4(X, L::off(row + 8, col));
   return cat8(lo, hi);
 }
 
 // MFMA operand whose k index runs along columns of a row-major LDS tile:
 // lane l receives X[row0 + l%32][col0 + 8*(l/32) + e], e = 0..7.
-__device__ __forceinline__ bf16x8 lds_frag_nat(const lds_bf16* X, int pitch, int row0, int col0) {
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag_nat(const lds_bf16* X, int row0, int col0) {
   const int l = lane_id();
-  return lds_read8(X, (row0 + (l & 31)) * pitch + col0 + 8 * (l >> 5));
+  return lds_read8(X, LdsLayout<D>::off(row0 + (l & 31), col0 + 8 * (l >> 5)));
 }
 
 // Exchange with the lane 32 positions away (the other half of a C column).

@@ -30,12 +30,13 @@ struct TileStage {
     }
   }
 
-  __device__ __forceinline__ void store(lds_bf16* lds, int pitch) const {
+  // store into a tile with the LdsLayout<D> arrangement
+  __device__ __forceinline__ void store(lds_bf16* lds) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = threadIdx.x + p * NTHR;
       const int row = idx / CPR, ch = idx % CPR;
-      lds_store16(lds + row * pitch + ch * 8, buf[p]);
+      lds_store16(lds + LdsLayout<D>::off(row, ch * 8), buf[p]);
     }
   }
 };
