@@ -46,8 +46,9 @@ def flops(cfg, n_ord=None, n_frz=None, B=None):
         "bwd_kv_frz": P * d * 2 * B * n_frz,  # dV = W^T dO
         "bwd_q": P * d * 2 * B * n_ord,       # dQ
     }
-    f["fwd"] = f["fwd_ord"] + f["fwd_frz"]
-    f["bwd"] = f["bwd_kv_ord"] + f["bwd_kv_frz"] + f["bwd_q"]
+    f["fwd"] = f["fwd_ord"] + f["fwd_frz"]        # one mixed-head launch
+    f["bwd_kv"] = f["bwd_kv_ord"] + f["bwd_kv_frz"]  # one mixed-head launch
+    f["bwd"] = f["bwd_kv"] + f["bwd_q"]
     f["total"] = f["fwd"] + f["bwd"]
     return f
 
@@ -140,9 +141,8 @@ def main():
     ws = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
     has_frz = any(fz)
     has_ord = not all(fz)
-    names_f = (["lognorm"] if has_frz else []) + (["fwd_ord"] if has_ord else []) + (["fwd_frz"] if has_frz else [])
-    names_b = ["bwd_pre"] + (["bwd_kv_ord"] if has_ord else []) + (["bwd_kv_frz"] if has_frz else []) \
-        + (["bwd_q"] if has_ord else [])
+    names_f = (["lognorm"] if has_frz else []) + ["fwd"]
+    names_b = ["bwd_pre", "bwd_kv"] + (["bwd_q"] if has_ord else [])
     n_fwd_ev = len(names_f) + 1
     n_bwd_ev = len(names_b) + 1
     stream = torch.cuda.current_stream()

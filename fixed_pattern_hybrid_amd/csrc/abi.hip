@@ -188,14 +188,8 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
     if (stg.mark() != hipSuccess) return SAF_EHIP;
   }
   if (p->dtype == SAF_BF16) {
-    if (n_ord > 0) {
-      if (saf::launch_fwd_ord_bf16(args, p->D, stream) != hipSuccess) return SAF_EHIP;
-      if (stg.mark() != hipSuccess) return SAF_EHIP;
-    }
-    if (n_frz > 0) {
-      if (saf::launch_fwd_frz_bf16(args, p->D, stream) != hipSuccess) return SAF_EHIP;
-      if (stg.mark() != hipSuccess) return SAF_EHIP;
-    }
+    if (saf::launch_fwd_bf16(args, p->D, stream) != hipSuccess) return SAF_EHIP;
+    if (stg.mark() != hipSuccess) return SAF_EHIP;
   } else {
     if (saf::launch_fwd_f32(args, p->D, stream) != hipSuccess) return SAF_EHIP;
     if (stg.mark() != hipSuccess) return SAF_EHIP;
@@ -256,14 +250,8 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
     // delta + zero frozen dQ/dK, key-block passes, query-block pass
     e = saf::launch_bwd_pre_bf16(args, p->D, stream);
     if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-    if (n_ord > 0) {
-      e = saf::launch_bwd_kv_ord_bf16(args, p->D, stream);
-      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-    }
-    if (n_frz > 0) {
-      e = saf::launch_bwd_kv_frz_bf16(args, p->D, stream);
-      if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-    }
+    e = saf::launch_bwd_kv_bf16(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
     if (n_ord > 0) {
       e = saf::launch_bwd_q_bf16(args, p->D, stream);
       if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;

@@ -12,9 +12,9 @@
 //
 // Kernels:
 //   bwd_pre : delta for ordinary heads; +0.0 into frozen heads' dQ, dK.
-//   bwd_kv  : one program per (b, h, 128-key block) for ordinary heads and
-//             per (h, 128-key block, batch group) for frozen heads; queries
-//             in tiles of 64.  Accumulators are dV^T and dK^T so that each
+//   bwd_kv  : one launch; one program per (b, h, 128-key block) for ordinary
+//             heads and per (h, 128-key block, batch group) for frozen heads;
+//             queries in tiles of 64.  Accumulators are dV^T and dK^T so that each
 //             lane owns one key and the C registers of S feed the products.
 //   bwd_q   : one program per (b, h, 128-query block) of ordinary heads;
 //             keys in tiles of 64; accumulator dQ^T.
@@ -112,14 +112,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
 // Key-block pass, ordinary head (b, h, kb).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void bwd_kv_ord_kernel(BwdArgs A) {
+__device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, lds_bf16* smem) {
   using C = BwdCfg<D>;
-  SAF_DYN_LDS(smem);
-  const int per_k = A.B * A.n_ord;
-  const int kb = blockIdx.x / per_k;  // key block 0 has the most queries: first
-  const int rem = blockIdx.x - kb * per_k;
-  const int b = rem / A.n_ord;
-  const int h = A.ord_heads[rem - b * A.n_ord];
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
@@ -257,15 +251,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void bwd_kv_ord_kernel
 // Key-block pass, frozen head (h, kb, batch group): dV = W^T dO.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
+__device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, lds_bf16* smem) {
   using C = BwdCfg<D>;
   constexpr int G = C::G;
-  SAF_DYN_LDS(smem);
-  const int per_k = A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / per_k;
-  const int rem = blockIdx.x - kb * per_k;
-  const int h = A.frz_heads[rem / A.n_groups];
-  const int grp = rem % A.n_groups;
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
@@ -373,6 +361,24 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_frz_kernel(BwdArgs A) {
 #pragma unroll
   for (int gb = 0; gb < G; ++gb)
     if (gb < nb) store_rows_t<D>(A.dv, b0 + gb, h, j, T, dva[gb], 1.f);
+}
+
+// Key-block pass for every head in one launch: program p -> (key block, slot),
+// key block 0 (the most queries) first; the slot's list selects the body.
+template <int D>
+__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void bwd_kv_kernel(BwdArgs A) {
+  SAF_DYN_LDS(smem);
+  const int n_ord_prog = A.B * A.n_ord;
+  const int per_k = n_ord_prog + A.n_frz * A.n_groups;
+  const int kb = blockIdx.x / per_k;
+  const int rem = blockIdx.x - kb * per_k;
+  if (rem < n_ord_prog) {
+    const int b = rem / A.n_ord;
+    kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], kb, smem);
+  } else {
+    const int f = rem - n_ord_prog;
+    kv_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, kb, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -500,27 +506,17 @@ hipError_t set_lds(K kernel, size_t bytes) {
 }
 
 template <int D>
-hipError_t launch_kv_d(BwdArgs args, hipStream_t stream, int which) {
+hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
   using C = BwdCfg<D>;
-  static_assert(C::kv_ord_lds <= 160 * 1024 && C::kv_frz_lds <= 160 * 1024, "LDS budget");
-  static const hipError_t a1 = set_lds(bwd_kv_ord_kernel<D>, C::kv_ord_lds);
-  static const hipError_t a2 = set_lds(bwd_kv_frz_kernel<D>, C::kv_frz_lds);
-  if (a1 != hipSuccess) return a1;
-  if (a2 != hipSuccess) return a2;
+  static_assert(C::kv_lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = set_lds(bwd_kv_kernel<D>, C::kv_lds);
+  if (attr != hipSuccess) return attr;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
-  if (which == 0) {
-    const int64_t grid = (int64_t)args.B * args.n_ord * args.nkb;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_kv_ord_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_ord_lds,
-                       stream, args);
-  } else {
-    const int64_t grid = (int64_t)args.n_frz * args.n_groups * args.nkb;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(bwd_kv_frz_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_frz_lds,
-                       stream, args);
-  }
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_lds, stream, args);
   return hipGetLastError();
 }
 
@@ -548,20 +544,13 @@ hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream) {
   }
 }
 
-static hipError_t launch_kv_which(const BwdArgs& args, int D, hipStream_t stream, int which) {
+hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream) {
   switch (D) {
-    case 64: return launch_kv_d<64>(args, stream, which);
-    case 96: return launch_kv_d<96>(args, stream, which);
-    case 128: return launch_kv_d<128>(args, stream, which);
+    case 64: return launch_kv_d<64>(args, stream);
+    case 96: return launch_kv_d<96>(args, stream);
+    case 128: return launch_kv_d<128>(args, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_bwd_kv_ord_bf16(const BwdArgs& args, int D, hipStream_t stream) {
-  return launch_kv_which(args, D, stream, 0);
-}
-hipError_t launch_bwd_kv_frz_bf16(const BwdArgs& args, int D, hipStream_t stream) {
-  return launch_kv_which(args, D, stream, 1);
 }
 
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream) {

@@ -10,10 +10,10 @@
 //     row normalisers, then multiplied with the value tiles of every batch
 //     element of the group.  The weights do not depend on the batch index,
 //     so one rebuild serves the whole group.
-// Outputs are written in the original head order.  The two kinds run as two
-// kernels on the caller's stream: on gfx950 registers are allocated per
-// kernel, and the frozen programs' per-batch accumulators would otherwise
-// lower the occupancy of the ordinary programs.
+// Outputs are written in the original head order.  Both kinds run in one
+// launch; with accumulators in VGPRs and batch groups of two, the two program
+// bodies need about the same registers and LDS, so sharing a launch costs no
+// occupancy and lets the few frozen programs fill gaps in the schedule.
 //
 // Work layout: 4 waves, 32 queries per wave, key tiles of 64.  Products are
 // computed transposed (S^T = K Q^T, O^T = V^T P^T) so that every lane owns
@@ -68,19 +68,12 @@ __device__ __forceinline__ void store_out_rows(const TensorRef& o, int b, int h,
 }
 
 // ---------------------------------------------------------------------------
-// Ordinary heads: causal softmax attention with an online row maximum.
-// Grid: nqb * B * n_ord programs, longest query blocks first.
+// Ordinary head program (b, h, query block): causal softmax attention with an
+// online row maximum.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
+__device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int qb, lds_bf16* smem) {
   using C = FwdCfg<D>;
-  SAF_DYN_LDS(smem);
-  const int per_q = A.B * A.n_ord;
-  const int qrank = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qrank * per_q;
-  const int qb = A.nqb - 1 - qrank;
-  const int b = rem / A.n_ord;
-  const int h = A.ord_heads[rem - b * A.n_ord];
 
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
@@ -212,20 +205,13 @@ __global__ __launch_bounds__(kThreads) void fwd_ord_kernel(FwdArgs A) {
 }
 
 // ---------------------------------------------------------------------------
-// Frozen heads: W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
-// Grid: nqb * n_frz * n_groups programs, longest query blocks first.
+// Frozen head program (h, query block, batch group):
+// W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
+__device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, lds_bf16* smem) {
   using C = FwdCfg<D>;
   constexpr int G = C::G;
-  SAF_DYN_LDS(smem);
-  const int per_q = A.n_frz * A.n_groups;
-  const int qrank = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qrank * per_q;
-  const int qb = A.nqb - 1 - qrank;
-  const int h = A.frz_heads[rem / A.n_groups];
-  const int grp = rem % A.n_groups;
 
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
@@ -335,51 +321,53 @@ __global__ __launch_bounds__(kThreads) void fwd_frz_kernel(FwdArgs A) {
     if (gb < nb) store_out_rows<D>(A.o, b0 + gb, h, i, T, oacc[gb], 1.f);
 }
 
-template <typename K>
-hipError_t set_lds(K kernel, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+// One launch for every head: program p -> (query block rank, slot); each
+// query block rank holds B * n_ord ordinary and n_frz * n_groups frozen
+// programs, and ranks run longest query blocks first.  The head-state flag
+// (which list the slot falls in) selects the program body.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs A) {
+  SAF_DYN_LDS(smem);
+  const int n_ord_prog = A.B * A.n_ord;
+  const int per_q = n_ord_prog + A.n_frz * A.n_groups;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
+  const int qb = A.nqb - 1 - qrank;
+  if (rem < n_ord_prog) {
+    const int b = rem / A.n_ord;
+    fwd_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], qb, smem);
+  } else {
+    const int f = rem - n_ord_prog;
+    fwd_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, qb, smem);
+  }
 }
 
 template <int D>
-hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream, int which) {
+hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
   using C = FwdCfg<D>;
-  static_assert(C::ord_lds <= 160 * 1024 && C::frz_lds <= 160 * 1024, "LDS budget");
-  static const hipError_t a1 = set_lds(fwd_ord_kernel<D>, C::ord_lds);
-  static const hipError_t a2 = set_lds(fwd_frz_kernel<D>, C::frz_lds);
-  if (a1 != hipSuccess) return a1;
-  if (a2 != hipSuccess) return a2;
+  constexpr size_t lds = C::ord_lds > C::frz_lds ? C::ord_lds : C::frz_lds;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(fwd_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nqb = (args.T + kBM - 1) / kBM;
-  if (which == 0) {
-    const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_ord_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::ord_lds, stream, args);
-  } else {
-    const int64_t grid = (int64_t)args.n_frz * args.n_groups * args.nqb;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fwd_frz_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::frz_lds, stream, args);
-  }
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nqb;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(kThreads), lds, stream, args);
   return hipGetLastError();
-}
-
-hipError_t launch_fwd_which(const FwdArgs& args, int D, hipStream_t stream, int which) {
-  switch (D) {
-    case 64: return launch_fwd_d<64>(args, stream, which);
-    case 96: return launch_fwd_d<96>(args, stream, which);
-    case 128: return launch_fwd_d<128>(args, stream, which);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace
 
-hipError_t launch_fwd_ord_bf16(const FwdArgs& args, int D, hipStream_t stream) {
-  return launch_fwd_which(args, D, stream, 0);
-}
-hipError_t launch_fwd_frz_bf16(const FwdArgs& args, int D, hipStream_t stream) {
-  return launch_fwd_which(args, D, stream, 1);
+hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream) {
+  switch (D) {
+    case 64: return launch_fwd_d<64>(args, stream);
+    case 96: return launch_fwd_d<96>(args, stream);
+    case 128: return launch_fwd_d<128>(args, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace saf

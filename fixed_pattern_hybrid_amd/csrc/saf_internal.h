@@ -71,12 +71,10 @@ hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const floa
 
 hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
 
-// bf16 path: ordinary and frozen heads run as separate kernels.
-hipError_t launch_fwd_ord_bf16(const FwdArgs& args, int D, hipStream_t stream);
-hipError_t launch_fwd_frz_bf16(const FwdArgs& args, int D, hipStream_t stream);
+// bf16 path: one mixed-head launch for the forward and for the key-block pass.
+hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream);
-hipError_t launch_bwd_kv_ord_bf16(const BwdArgs& args, int D, hipStream_t stream);
-hipError_t launch_bwd_kv_frz_bf16(const BwdArgs& args, int D, hipStream_t stream);
+hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream);
 
 // fp32 path: one kernel per pass covers both head kinds.
