@@ -53,6 +53,105 @@ def flops(cfg, n_ord=None, n_frz=None, B=None):
     return f
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_kv_gpt2-124m-layer_B8_T4096_d64_25pct.txt")
+KERNEL_SOURCES = ("kern_bwd.hip", "saf_device.h", "saf_tile.h", "saf_internal.h")
+
+
+def kernel_source_sha() -> str:
+    """Hash of the sources the key-block kernel is compiled from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "fixed_pattern_hybrid_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it was taken on other kernel sources (or is absent)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel") != kernel or kv.get("source_sha") != kernel_source_sha():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calib_copy(n_mib: int = 1024, reps: int = 5):
+    """A plain device copy of known size, for scaling FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = n_mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "reps": reps}), flush=True)
+
+
+def per_head_costs(B, cfg, reps: int = 10):
+    """Per-head fwd and fwd+bwd cost at the workload's shape with every head
+    ordinary versus every head frozen, timed in A-B-B-A order."""
+    import numpy as np
+    import torch
+
+    from synth import make_inputs
+
+    res = {}
+    for kind, fz_set in (("ordinary", ()), ("frozen", tuple(range(cfg.H)))):
+        c = cfg.with_(frozen=fz_set)
+        inp = make_inputs(c)
+        dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda().to(torch.bfloat16)  # noqa: E731
+        t = dict(q=dev(inp.q), k=dev(inp.k), v=dev(inp.v), do=dev(inp.do),
+                 a=torch.from_numpy(inp.a).cuda(), r=torch.from_numpy(inp.r).cuda(),
+                 fz=[int(x) for x in inp.frozen])
+        t["o"] = torch.empty_like(t["v"])
+        t["lse"] = torch.empty((c.B, c.H, c.T), dtype=torch.float32, device="cuda")
+        t["g"] = [torch.empty_like(t["v"]) for _ in range(3)]
+        prm = B.Params(t["v"], t["fz"], inp.a.shape[1])
+        t["ws"] = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
+        res[kind] = t
+
+    def run(t, with_bwd):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            B.saf_hybrid_attn_fwd(t["q"], t["k"], t["v"], t["fz"], t["a"], t["r"], out=t["o"], lse=t["lse"])
+            if with_bwd:
+                B.saf_hybrid_attn_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["fz"], t["a"], t["r"],
+                                      dq=t["g"][0], dk=t["g"][1], dv=t["g"][2], workspace=t["ws"])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    out = {}
+    for with_bwd, tag in ((False, "fwd"), (True, "fwd_bwd")):
+        run(res["ordinary"], with_bwd)
+        run(res["frozen"], with_bwd)
+        samples = {"ordinary": [], "frozen": []}
+        for order in (("ordinary", "frozen"), ("frozen", "ordinary")) * 2:
+            for kind in order:
+                samples[kind].append(run(res[kind], with_bwd))
+        o_ms = float(np.median(samples["ordinary"])) / cfg.H
+        f_ms = float(np.median(samples["frozen"])) / cfg.H
+        out[tag] = {"ordinary_ms_per_head": round(o_ms, 5), "frozen_ms_per_head": round(f_ms, 5),
+                    "frozen_over_ordinary": round(f_ms / o_ms, 3)}
+    out["note"] = (f"same shape (B={cfg.B}, T={cfg.T}, d={cfg.D}), all {cfg.H} heads ordinary vs all frozen; "
+                   "median of 4 A/B/B/A-ordered samples of 10 calls each")
+    return out
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     """Time the float64 oracle on whole heads of the workload (host cores)."""
     import numpy as np
@@ -113,11 +212,18 @@ def main():
     ap.add_argument("--config", default="gpt2_124m_4k_25pct")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-per-head", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is not built "
                                    "(--gpus must be 1)"}))
         sys.exit(2)
+
+    if args.calib_copy:
+        calib_copy()
+        return
 
     import numpy as np
     import torch
@@ -197,8 +303,9 @@ def main():
     roof = None
     if dom_flops is not None:
         ach = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
+        traffic = measured_traffic(f"bwd_kv_kernel<{D}>") if dom == "bwd_kv" else None
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": dom,
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
                 "kernel_ms": round(kern_ms[dom], 4)}
     out = {
         "metric": "hybrid-attn fwd+bwd TFLOP/s & MFMA util, 124M/4K shape, 25% heads frozen",
@@ -221,6 +328,8 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
+    if not args.no_per_head and do is not None:
+        out["per_head"] = per_head_costs(B, cfg)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)
