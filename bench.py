@@ -120,14 +120,16 @@ def per_head_costs(B, cfg, reps: int = 10):
         t["lse"] = torch.empty((c.B, c.H, c.T), dtype=torch.float32, device="cuda")
         t["g"] = [torch.empty_like(t["v"]) for _ in range(3)]
         prm = B.Params(t["v"], t["fz"], inp.a.shape[1])
-        t["ws"] = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
+        t["ws"] = torch.empty(max(B.workspace_bytes(prm, True), B.workspace_bytes(prm, False), 256),
+                              dtype=torch.uint8, device="cuda")
         res[kind] = t
 
     def run(t, with_bwd):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            B.saf_hybrid_attn_fwd(t["q"], t["k"], t["v"], t["fz"], t["a"], t["r"], out=t["o"], lse=t["lse"])
+            B.saf_hybrid_attn_fwd(t["q"], t["k"], t["v"], t["fz"], t["a"], t["r"], out=t["o"], lse=t["lse"],
+                                  workspace=t["ws"])
             if with_bwd:
                 B.saf_hybrid_attn_bwd(t["q"], t["k"], t["v"], t["o"], t["do"], t["lse"], t["fz"], t["a"], t["r"],
                                       dq=t["g"][0], dk=t["g"][1], dv=t["g"][2], workspace=t["ws"])
@@ -166,27 +168,29 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
         threads = os.cpu_count() or 1
     s = 1.0 / np.sqrt(cfg.D)
     fz = [int(x) for x in inp.frozen]
-    # alternate ordinary / frozen heads of batch element 0 until the budget is used
-    order = []
+    # alternate ordinary / frozen heads, batch element by batch element, until
+    # the budget is used
     ords = [h for h in range(cfg.H) if not fz[h]]
     frzs = [h for h in range(cfg.H) if fz[h]]
-    for x in range(max(len(ords), len(frzs))):
-        if x < len(ords):
-            order.append(ords[x])
-        if x < len(frzs):
-            order.append(frzs[x])
+    order = []
+    for b in range(cfg.B):
+        for x in range(max(len(ords), len(frzs))):
+            if x < len(ords):
+                order.append((b, ords[x]))
+            if x < len(frzs):
+                order.append((b, frzs[x]))
     done_ord = done_frz = 0
     t0 = time.perf_counter()
-    for h in order:
+    for b, h in order:
         if fz[h]:
-            oracle.frozen_head_fwd(inp.v[0, h], inp.a[h], inp.r[h])
+            oracle.frozen_head_fwd(inp.v[b, h], inp.a[h], inp.r[h])
             if inp.do is not None:
-                oracle.frozen_head_bwd(inp.do[0, h], inp.a[h], inp.r[h])
+                oracle.frozen_head_bwd(inp.do[b, h], inp.a[h], inp.r[h])
             done_frz += 1
         else:
-            oracle.ordinary_head_fwd(inp.q[0, h], inp.k[0, h], inp.v[0, h], s)
+            oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], s)
             if inp.do is not None:
-                oracle.ordinary_head_bwd(inp.q[0, h], inp.k[0, h], inp.v[0, h], inp.do[0, h], s)
+                oracle.ordinary_head_bwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], s)
             done_ord += 1
         if time.perf_counter() - t0 >= budget_s and done_ord and done_frz:
             break
@@ -198,8 +202,9 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"float64 dense oracle, fwd+bwd of {done_ord} ordinary + {done_frz} frozen whole heads "
-                  f"(b=0, T={cfg.T}, d={cfg.D}) in {dt:.1f} s; value = their algorithmic flops / time",
+        "sample": f"float64 dense oracle, fwd+bwd of {done_ord} ordinary + {done_frz} frozen whole "
+                  f"(batch, head) slices (T={cfg.T}, d={cfg.D}) in {dt:.1f} s; "
+                  f"value = their algorithmic flops / time",
         "seconds": round(dt, 2),
     }
 
@@ -244,7 +249,8 @@ def main():
     lse = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
     dq, dk, dv = torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)
     prm = B.Params(v, fz, a.shape[1])
-    ws = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(B.workspace_bytes(prm, True), B.workspace_bytes(prm, False), 256),
+                     dtype=torch.uint8, device="cuda")
     has_frz = any(fz)
     has_ord = not all(fz)
     names_f = (["lognorm"] if has_frz else []) + ["fwd"]
@@ -260,7 +266,7 @@ def main():
         return evs
 
     def step(fe=None, be=None):
-        B.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=o, lse=lse, stream=stream, events=fe)
+        B.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=o, lse=lse, workspace=ws, stream=stream, events=fe)
         if do is not None:
             B.saf_hybrid_attn_bwd(q, k, v, o, do, lse, fz, a, r, dq=dq, dk=dk, dv=dv, workspace=ws,
                                   stream=stream, events=be)

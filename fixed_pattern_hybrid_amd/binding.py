@@ -176,7 +176,7 @@ def workspace_bytes(params: Params, for_bwd: bool) -> int:
 
 
 def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse=None,
-                        stream=None, events=None):
+                        workspace=None, stream=None, events=None):
     """Forward of the hybrid layer; returns (O, lse).
 
     q, k, v: [B, H, T, D] bf16 or fp32 CUDA tensors (unit stride on D);
@@ -194,7 +194,10 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     prm = Params(v, frozen, a.shape[1], softmax_scale, events)
     prm.set_strides(q=q, k=k, v=v, o=out)
     ws_n = workspace_bytes(prm, False)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
+    if workspace is not None:
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
     st = LIB.saf_hybrid_attn_fwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(r), _ptr(out),
                                  _ptr(lse), _ptr(ws), ws_n, _stream_handle(stream))
     _check(st, "saf_hybrid_attn_fwd")

@@ -86,6 +86,15 @@ size_t bwd_ws_bytes(const saf_attn_params* p) {
   return round_up((size_t)p->B * p->H * p->T * sizeof(float), 256);
 }
 
+int lognorm_chunks(int T) { return (T + saf::kLognormChunk - 1) / saf::kLognormChunk; }
+
+// bf16 forward with frozen heads: per-chunk normaliser partials, one float2
+// per (frozen head, key chunk, row).  The fp32 forward needs none.
+size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
+  if (p->dtype != SAF_BF16 || n_frz == 0) return 0;
+  return round_up((size_t)n_frz * lognorm_chunks(p->T) * p->T * 2 * sizeof(float), 256);
+}
+
 // Records stage event k when the caller asked for it.
 struct Stages {
   const saf_attn_params* p;
@@ -131,14 +140,12 @@ int32_t saf_version(void) { return kVersion; }
 size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd) {
   int o, f;
   if (check_params(p, &o, &f) != SAF_OK) return 0;
-  return for_bwd ? bwd_ws_bytes(p) : 0;
+  return for_bwd ? bwd_ws_bytes(p) : fwd_ws_bytes(p, f);
 }
 
 int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
                         const float* a, const float* r, void* o, float* lse, void* ws,
                         size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;  // the forward needs no workspace
   int n_ord = 0, n_frz = 0;
   int st = check_params(p, &n_ord, &n_frz);
   if (st != SAF_OK) return st;
@@ -150,6 +157,8 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
   if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
   if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
+  const size_t need = fwd_ws_bytes(p, n_frz);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return SAF_EWORKSPACE;
 
   FwdArgs args;
   std::memset(&args, 0, sizeof(args));
@@ -184,7 +193,15 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
     la.T = p->T;
     la.prior_len = p->prior_len;
     std::memcpy(la.heads, args.frz_heads, sizeof(la.heads));
-    if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;
+    if (p->dtype == SAF_BF16) {
+      // partials only; the forward's frozen programs merge them and write lse
+      args.lz_part = static_cast<const float2*>(ws);
+      args.n_chunks = lognorm_chunks(p->T);
+      if (saf::launch_lognorm_partial(la, static_cast<float2*>(ws), stream) != hipSuccess)
+        return SAF_EHIP;
+    } else {
+      if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;
+    }
     if (stg.mark() != hipSuccess) return SAF_EHIP;
   }
   if (p->dtype == SAF_BF16) {

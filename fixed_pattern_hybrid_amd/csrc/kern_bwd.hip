@@ -75,37 +75,49 @@ __device__ __forceinline__ float bf16hi(unsigned u) { return __builtin_bit_cast(
 
 // ---------------------------------------------------------------------------
 // delta = rowsum(dO * O) (ordinary heads); zero dQ, dK (frozen heads).
-// Grid: (ceil(T/256), B*H); one thread per row.
+// Grid: (ceil(T/32), B*H); eight lanes per row, each taking 16-byte chunks
+// c, c+8, ... of the row, so a wave reads eight whole rows contiguously.
 // ---------------------------------------------------------------------------
+constexpr int kPreLPR = 8;                // lanes per row
+constexpr int kPreRows = 256 / kPreLPR;  // rows per block
+
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
+  constexpr int NCH = D / 8;  // 16-byte chunks per row
   const int bh = blockIdx.y;
   const int b = bh / A.H, h = bh - b * A.H;
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= A.T) return;
+  const int sub = threadIdx.x % kPreLPR;
+  const int i = blockIdx.x * kPreRows + threadIdx.x / kPreLPR;
+  const bool live = i < A.T;  // every lane of a row group shares it
   if (A.is_frozen[h]) {
+    if (!live) return;
     __bf16* dq = (__bf16*)A.dq.ptr + (int64_t)b * A.dq.sb + (int64_t)h * A.dq.sh + (int64_t)i * A.dq.st;
     __bf16* dk = (__bf16*)A.dk.ptr + (int64_t)b * A.dk.sb + (int64_t)h * A.dk.sh + (int64_t)i * A.dk.st;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) {
+    for (int c = sub; c < NCH; c += kPreLPR) {
       sstore16(dq + 8 * c, u32x4{0u, 0u, 0u, 0u});
       sstore16(dk + 8 * c, u32x4{0u, 0u, 0u, 0u});
     }
     return;
   }
-  const __bf16* o = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
-  const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh + (int64_t)i * A.dout.st;
   float acc = 0.f;
+  if (live) {
+    const __bf16* o = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
+    const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh + (int64_t)i * A.dout.st;
 #pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 x = gload16(o + 8 * c), y = gload16(g + 8 * c);
+    for (int c = sub; c < NCH; c += kPreLPR) {
+      const u32x4 x = gload16(o + 8 * c), y = gload16(g + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf16lo(x[e]), bf16lo(y[e]), acc);
-      acc = fmaf(bf16hi(x[e]), bf16hi(y[e]), acc);
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf16lo(x[e]), bf16lo(y[e]), acc);
+        acc = fmaf(bf16hi(x[e]), bf16hi(y[e]), acc);
+      }
     }
   }
-  A.delta[((int64_t)b * A.H + h) * A.T + i] = acc;
+  // row groups are aligned 8-lane groups of the wave
+#pragma unroll
+  for (int m = 1; m < kPreLPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+  if (live && sub == 0) A.delta[((int64_t)b * A.H + h) * A.T + i] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -494,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
 
 template <int D>
 hipError_t launch_pre_d(const BwdArgs& args, hipStream_t stream) {
-  dim3 grid((args.T + 255) / 256, args.B * args.H);
+  dim3 grid((args.T + kPreRows - 1) / kPreRows, args.B * args.H);
   hipLaunchKernelGGL(bwd_pre_kernel<D>, grid, dim3(256), 0, stream, args);
   return hipGetLastError();
 }

@@ -209,7 +209,7 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
 // W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int h, int grp, int qb, lds_bf16* smem) {
+__device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, int qb, lds_bf16* smem) {
   using C = FwdCfg<D>;
   constexpr int G = C::G;
 
@@ -227,9 +227,27 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int h, int grp, int
   lds_f32* fbase = (lds_f32*)(smem + 2 * G * C::TILE);
   constexpr int FSTRIDE = C::FSTRIDE;
 
+  const int h = A.frz_heads[hidx];
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
-  const float z2 = (i < T) ? A.lse[((int64_t)b0 * A.H + h) * T + i] * kLog2e : 0.f;
+  // log N(i) in log2 units: merge the per-chunk partials of this row, and
+  // record it as the row's lse for every batch element of the group.
+  float z2 = 0.f;
+  if (i < T) {
+    float M = kNegInf, S = 0.f;
+    const float2* part = A.lz_part + (int64_t)hidx * A.n_chunks * T + i;
+    for (int c = 0; c <= i / kLognormChunk; ++c) {
+      const float2 p = part[(int64_t)c * T];
+      if (p.y > 0.f) {
+        const float Mn = fmaxf(M, p.x);
+        S = S * fast_exp2(M - Mn) + p.y * fast_exp2(p.x - Mn);
+        M = Mn;
+      }
+    }
+    z2 = M + fast_log2(S);
+    if (hl == 0)
+      for (int gb = 0; gb < nb; ++gb) A.lse[((int64_t)(b0 + gb) * A.H + h) * T + i] = z2 * kLn2;
+  }
 
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
@@ -338,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs A) {
     fwd_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], qb, smem);
   } else {
     const int f = rem - n_ord_prog;
-    fwd_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, qb, smem);
+    fwd_frozen<D>(A, f / A.n_groups, f % A.n_groups, qb, smem);
   }
 }
 

@@ -8,6 +8,7 @@
 namespace saf {
 
 constexpr int kMaxHeads = 256;
+constexpr int kLognormChunk = 1024;  // keys per normaliser partial
 
 // One strided [B][H][T][D] tensor: base pointer and element strides of
 // (b, h, t); the d stride is 1.
@@ -28,6 +29,10 @@ struct FwdArgs {
   int frz_group;     // batch elements per frozen program
   int n_groups;      // ceil(B / frz_group)
   int nqb;           // number of query blocks
+  // bf16 path: per-chunk normaliser partials (max, sum) in log2 units,
+  // [n_frz][n_chunks][T]; the frozen programs merge them and write lse.
+  const float2* lz_part;
+  int n_chunks;
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
 };
@@ -66,6 +71,7 @@ struct LognormArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream);
+hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, hipStream_t stream);
 hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const float* r, float* w,
                                 hipStream_t stream);
 

@@ -109,8 +109,13 @@ typedef struct saf_attn_params {
  *   o       : device [B][H][T][D] output.
  *   lse     : device fp32 [B][H][T] output (see conventions above).
  *   ws      : workspace of at least saf_hybrid_attn_workspace_bytes(p, 0)
- *             bytes, 256-byte aligned (may be NULL when that is 0).
- * Kernels: the frozen heads' row normalisers, then one mixed-head launch.
+ *             bytes, 256-byte aligned (may be NULL when that is 0).  bf16
+ *             with frozen heads needs n_frozen * ceil(T / 1024) * T * 8
+ *             bytes (rounded up to 256) for per-key-chunk partial sums of
+ *             the row normalisers; fp32, or no frozen head, needs none.
+ *             Contents on entry are ignored and left undefined on return.
+ * Kernels: the frozen heads' row normalisers (bf16: chunk partials, merged
+ * by the frozen programs of the next launch), then one mixed-head launch.
  */
 int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k,
                         const void* v, const float* a, const float* r, void* o,

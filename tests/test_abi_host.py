@@ -131,6 +131,21 @@ def test_bwd_workspace_checks(b):
     assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(bad), 1) == 0
 
 
+def test_fwd_workspace_checks(b):
+    T = 2100  # three key chunks of 1024
+    p, arr = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1])
+    need = b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0)
+    assert need == -(-(2 * 3 * T * 8) // 256) * 256
+    args = [FAKE] * 7
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, None, need, None) == -3
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE, need - 1, None) == -3
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE + 16, need, None) == -3
+    p32, arr32 = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1], dtype=b.SAF_F32)
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p32), 0) == 0
+    pord, arro = _params(b, B=2, H=4, T=T)
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(pord), 0) == 0
+
+
 def test_pattern_entry_points_reject(b):
     assert b.LIB.saf_pattern_dense(0, 4, FAKE, FAKE, FAKE, None) == -1
     assert b.LIB.saf_pattern_dense(8, 4, FAKE, FAKE, FAKE, None) == -1
