@@ -154,29 +154,33 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     }
   }
 
-  // LDS: Q[buf] at buf*TILE, dO[buf] at (2+buf)*TILE, then lse2[buf], delta[buf]
+  // LDS: Q[buf] at buf*TILE, dO[buf] at (2+buf)*TILE, then lse2[buf] and
+  // -delta[buf] (the negated delta seeds the dP accumulator).
   lds_f32* fb = (lds_f32*)(smem + 4 * C::TILE);
 
-  const int qt0 = k0 / kKvBM;
+  const int qt0 = k0 / kKvBM;  // < nqt since k0 < T
   const int nqt = (T + kKvBM - 1) / kKvBM;
 
+  // Next-tile operands are loaded into registers at the start of a tile and
+  // written to LDS at its end.
   TileStage<D, kKvBM, kThreads> qst, ost;
-  auto stage_vec = [&](int i0, int buf) {
-    lds_f32* ls = fb + buf * kKvBM;
-    lds_f32* ds = fb + (2 + buf) * kKvBM;
-    for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
-      const int i = i0 + x;
-      ls[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();  // padding rows: P = 0
-      ds[x] = (i < T) ? dl[i] : 0.f;
+  ScalarStage lsv, dlv;
+  auto load_next = [&](int i0) {
+    qst.load(qg, A.q.st, i0, T);
+    ost.load(dog, A.dout.st, i0, T);
+    lsv.load(lse, i0, T);
+    dlv.load(dl, i0, T);
+  };
+  auto store_next = [&](int buf) {
+    qst.store(smem + buf * C::TILE);
+    ost.store(smem + (2 + buf) * C::TILE);
+    if (threadIdx.x < kKvBM) {
+      fb[buf * kKvBM + threadIdx.x] = lsv.valid ? lsv.v * kLog2e : __builtin_inff();  // padding: P = 0
+      fb[(2 + buf) * kKvBM + threadIdx.x] = dlv.valid ? -dlv.v : 0.f;
     }
   };
-  if (qt0 < nqt) {
-    qst.load(qg, A.q.st, qt0 * kKvBM, T);
-    ost.load(dog, A.dout.st, qt0 * kKvBM, T);
-    qst.store(smem);
-    ost.store(smem + 2 * C::TILE);
-    stage_vec(qt0 * kKvBM, 0);
-  }
+  load_next(qt0 * kKvBM);
+  store_next(0);
   __syncthreads();
 
   f32x16 dva[C::NDB], dka[C::NDB];
@@ -194,20 +198,23 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
-    if (more) {
-      qst.load(qg, A.q.st, i0 + kKvBM, T);
-      ost.load(dog, A.dout.st, i0 + kKvBM, T);
-    }
+    if (more) load_next(i0 + kKvBM);
     const lds_bf16* Q = smem + bi * C::TILE;
     const lds_bf16* O = smem + (2 + bi) * C::TILE;
     const lds_f32* ls = fb + bi * kKvBM;
-    const lds_f32* ds = fb + (2 + bi) * kKvBM;
+    const lds_f32* nd = fb + (2 + bi) * kKvBM;
     if (!MASK || i0 + kKvBM - 1 >= wk_lo) {
+      // S = Q K^T and dP - delta = dO V^T - delta (accumulator seeded with -delta)
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         s[c] = f32x16{};
-        dp[c] = f32x16{};
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 d4 = lds_read_f4(nd + 32 * c + 8 * q4 + 4 * hl);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[c][4 * q4 + e] = d4[e];
+        }
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           s[c] = mfma32(lds_frag_nat<D>(Q, 32 * c, 16 * ks), kf[ks], s[c]);
@@ -220,7 +227,6 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
         for (int q4 = 0; q4 < 4; ++q4) {
           const int ib = 32 * c + 8 * q4 + 4 * hl;  // first of 4 consecutive tile rows
           const f32x4 l4 = lds_read_f4(ls + ib);
-          const f32x4 d4 = lds_read_f4(ds + ib);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * q4 + e;
@@ -229,7 +235,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
               if ((i0 + ib + e) < j) p = 0.f;
             }
             s[c][r] = p;
-            dp[c][r] = p * (dp[c][r] - d4[e]);
+            dp[c][r] = p * dp[c][r];
           }
         }
       // dV^T += dO^T P ; dK^T += Q^T dS
@@ -244,11 +250,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
         }
       }
     }
-    if (more) {
-      qst.store(smem + (bi ^ 1) * C::TILE);
-      ost.store(smem + (2 + (bi ^ 1)) * C::TILE);
-      stage_vec(i0 + kKvBM, bi ^ 1);
-    }
+    if (more) store_next(bi ^ 1);
     __syncthreads();
   };
   const int qt_full = min(qt0 + 2, nqt);
@@ -300,28 +302,25 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) ost[gb].store(smem + (buf * G + gb) * C::TILE);
   };
-  // z2 = log N (log2 units) of the tile rows; r band over offsets
-  // [i0 - k0 - (BN-1), i0 + BM - 1 - k0].
-  auto stage_pattern = [&](int i0, int buf) {
+  // Next-tile operands: dO tiles, z2 = log N (log2 units) of the tile rows,
+  // and the r band over offsets [i0 - k0 - (BN-1), i0 + BM - 1 - k0]; loaded
+  // into registers at the start of a tile, written to LDS at its end.
+  ScalarStage zv;
+  BandStage<C::BAND, kThreads> band;
+  auto load_next = [&](int i0) {
+    load_do(i0);
+    zv.load(lse, i0, T);
+    band.load(rrow, i0 - k0 - (kKvBN - 1), T);
+  };
+  auto store_next = [&](int buf) {
+    store_do(buf);
     lds_f32* zs = fb + buf * FSTRIDE;
-    lds_f32* rs = zs + kKvBM;
-    for (int x = threadIdx.x; x < kKvBM; x += kThreads) {
-      const int i = i0 + x;
-      zs[x] = (i < T) ? lse[i] * kLog2e : __builtin_inff();
-    }
-    const int dmin = i0 - k0 - (kKvBN - 1);
-    for (int x = threadIdx.x; x < 4 * C::BAND; x += kThreads) {
-      const int c = x / C::BAND, y = x - c * C::BAND;
-      const int d = dmin + y + c;
-      rs[x] = (y + c < C::BAND && d >= 0 && d < T) ? rrow[d] * kLog2e : kNegInf;
-    }
+    if (threadIdx.x < kKvBM) zs[threadIdx.x] = zv.valid ? zv.v * kLog2e : __builtin_inff();
+    band.store(zs + kKvBM);
   };
 
-  if (qt0 < nqt) {
-    load_do(qt0 * kKvBM);
-    store_do(0);
-    stage_pattern(qt0 * kKvBM, 0);
-  }
+  load_next(qt0 * kKvBM);  // qt0 < nqt since k0 < T
+  store_next(0);
   __syncthreads();
 
   f32x16 dva[G][C::NDB];
@@ -334,7 +333,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
-    if (more) load_do(i0 + kKvBM);
+    if (more) load_next(i0 + kKvBM);
     const lds_f32* zs = fb + bi * FSTRIDE;
     const lds_f32* rs = zs + kKvBM;
     if (i0 + kKvBM - 1 >= wk_lo) {
@@ -364,10 +363,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
                                  wf, dva[gb][db]);
       }
     }
-    if (more) {
-      store_do(bi ^ 1);
-      stage_pattern(i0 + kKvBM, bi ^ 1);
-    }
+    if (more) store_next(bi ^ 1);
     __syncthreads();
   }
 #pragma unroll

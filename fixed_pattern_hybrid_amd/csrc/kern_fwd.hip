@@ -236,12 +236,18 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   if (i < T) {
     float M = kNegInf, S = 0.f;
     const float2* part = A.lz_part + (int64_t)hidx * A.n_chunks * T + i;
-    for (int c = 0; c <= i / kLognormChunk; ++c) {
-      const float2 p = part[(int64_t)c * T];
-      if (p.y > 0.f) {
-        const float Mn = fmaxf(M, p.x);
-        S = S * fast_exp2(M - Mn) + p.y * fast_exp2(p.x - Mn);
-        M = Mn;
+    const int cmax = i / kLognormChunk;  // chunks 0..cmax hold this row's terms
+    for (int c0 = 0; c0 <= cmax; c0 += 4) {
+      float2 p[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p[u] = part[(int64_t)min(c0 + u, cmax) * T];  // four loads in flight
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c0 + u <= cmax && p[u].y > 0.f) {
+          const float Mn = fmaxf(M, p[u].x);
+          S = S * fast_exp2(M - Mn) + p[u].y * fast_exp2(p[u].x - Mn);
+          M = Mn;
+        }
       }
     }
     z2 = M + fast_log2(S);
@@ -252,39 +258,33 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
-  // a (log2 units) for the tile keys; band[x] = r2[dmin + x] for the offsets
-  // of the tile, -inf outside [0, T), in four shifted copies.
-  auto stage_pattern = [&](int j0, lds_f32* as) {
-    lds_f32* rs = as + kBN;
-    for (int x = threadIdx.x; x < kBN; x += kThreads) {
-      const int j = j0 + x;
-      as[x] = (j < T) ? arow[j] * kLog2e : kNegInf;
-    }
-    const int dmin = q0 - j0 - (kBN - 1);
-    for (int x = threadIdx.x; x < 4 * C::BAND; x += kThreads) {
-      const int c = x / C::BAND, y = x - c * C::BAND;
-      const int dl = dmin + y + c;
-      rs[x] = (y + c < C::BAND && dl >= 0 && dl < T) ? rrow[dl] * kLog2e : kNegInf;
-    }
-  };
-
+  // Next-tile operands, loaded into registers at the start of a tile and
+  // written to LDS at its end: the V tiles of the group, a (log2 units) of
+  // the tile keys (-inf for keys >= T) and the r band over the offsets of the
+  // tile, band[x] = r2[q0 - j0 - (BN-1) + x].
   TileStage<D, kBN, kThreads> vst[G];
-  auto load_v = [&](int j0) {
+  ScalarStage av;
+  BandStage<C::BAND, kThreads> band;
+  auto load_next = [&](int j0) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
       const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
       vst[gb].load(vg, A.v.st, j0, T);
     }
+    av.load(arow, j0, T);
+    band.load(rrow, q0 - j0 - (kBN - 1), T);
   };
-  auto store_v = [&](int buf) {
+  auto store_next = [&](int buf) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) vst[gb].store(smem + (buf * G + gb) * C::TILE);
+    lds_f32* as = fbase + buf * FSTRIDE;
+    if (threadIdx.x < kBN) as[threadIdx.x] = av.valid ? av.v * kLog2e : kNegInf;
+    band.store(as + kBN);
   };
 
-  load_v(0);
-  stage_pattern(0, fbase);
-  store_v(0);
+  load_next(0);
+  store_next(0);
   __syncthreads();
 
   f32x16 oacc[G][C::NDB];
@@ -296,7 +296,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
-    if (more) load_v(j0 + kBN);
+    if (more) load_next(j0 + kBN);
     const int buf = t & 1;
     const lds_f32* as = fbase + buf * FSTRIDE;
     const lds_f32* rs = as + kBN;
@@ -327,10 +327,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
                                   wf, oacc[gb][db]);
       }
     }
-    if (more) {
-      store_v(buf ^ 1);
-      stage_pattern(j0 + kBN, fbase + (buf ^ 1) * FSTRIDE);
-    }
+    if (more) store_next(buf ^ 1);
     __syncthreads();
   }
 
