@@ -64,6 +64,7 @@ int check_tensor(const void* ptr, const int64_t* s, const saf_attn_params* p) {
     if (s[x] % vec != 0) return SAF_EINVAL;
   }
   if (p->T > 1 && s[2] < p->D) return SAF_EINVAL;  // rows of one head may not overlap
+  if (s[2] > SAF_MAX_T_STRIDE) return SAF_EUNSUPPORTED;  // 32-bit tile offsets
   return SAF_OK;
 }
 

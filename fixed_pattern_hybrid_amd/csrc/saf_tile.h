@@ -5,12 +5,21 @@
 
 namespace saf {
 
-// A [ROWS][D] bf16 tile of a strided tensor, staged by NTHR threads in 16-byte
-// chunks: loaded into registers at the start of a tile, stored to LDS at its
-// end.  Rows at or beyond `T` read row T-1 (always in range, T >= 1) and are
-// replaced by zeros when stored.  The loads carry no branches and nothing
-// consumes them before the store, so the compiler neither waits for them
-// early nor serialises the compute that overlaps them.
+// Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
+// parts: 32-bit data format, so dword loads return the stored bits.
+constexpr int kBufferFlags = 0x00020000;
+
+// A [ROWS][D] bf16 tile of a strided tensor (rows row0 .., row stride `st`
+// elements, unit stride along D), staged by NTHR threads in 16-byte chunks:
+// loaded into registers at the start of a tile, stored to LDS at its end.
+//
+// The loads go through a buffer resource whose range ends after the last
+// row below T: chunks of rows >= T fall outside it and read as zero without
+// touching memory, so the loads carry no branches, clamps or selects, and the
+// 32-bit offsets are fixed per thread.  Nothing consumes a loaded register
+// before the store, so the compute of the tile overlaps the loads.
+// Offsets are row * st * 2 bytes (row < ROWS), which the host keeps below
+// 2^31 by bounding st.
 template <int D, int ROWS, int NTHR>
 struct TileStage {
   static constexpr int CPR = D / 8;  // 16-byte chunks per row
@@ -18,16 +27,22 @@ struct TileStage {
   static constexpr int PER = (CHUNKS + NTHR - 1) / NTHR;
   static_assert(CHUNKS % NTHR == 0, "tile must split evenly over the threads");
   u32x4 buf[PER];
-  bool in[PER];
 
   __device__ __forceinline__ void load(const __bf16* base, int64_t st, int row0, int T) {
+    // Rows of one head never overlap when T > 1 (st >= D); a one-row tensor
+    // may have any stride, and its missing rows use the stride D so that
+    // they still fall outside the range.
+    const int64_t ste = st > D ? st : D;
+    const int rows = T - row0 < ROWS ? T - row0 : ROWS;
+    const int nrec = rows >= 1 ? (int)((int64_t)(rows - 1) * ste * 2 + D * 2) : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)row0 * st), (short)0, nrec, kBufferFlags);
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int idx = threadIdx.x + p * NTHR;
       const int row = idx / CPR, ch = idx % CPR;
-      const int t = row0 + row;
-      in[p] = t < T;
-      buf[p] = gload16(base + (int64_t)(t < T ? t : T - 1) * st + ch * 8);
+      buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rsrc, row * (int)ste * 2 + ch * 16, 0, 0));
     }
   }
 
@@ -37,9 +52,7 @@ struct TileStage {
     for (int p = 0; p < PER; ++p) {
       const int idx = threadIdx.x + p * NTHR;
       const int row = idx / CPR, ch = idx % CPR;
-      const u32x4 v = buf[p];
-      lds_store16(lds + LdsLayout<D>::off(row, ch * 8),
-                  u32x4{in[p] ? v[0] : 0u, in[p] ? v[1] : 0u, in[p] ? v[2] : 0u, in[p] ? v[3] : 0u});
+      lds_store16(lds + LdsLayout<D>::off(row, ch * 8), buf[p]);
     }
   }
 };

@@ -27,7 +27,8 @@
  *  - Q, K, V, O, dO, dQ, dK, dV have logical shape [B][H][T][D].  Their
  *    element strides for (b, h, t) are given per tensor; the stride of the
  *    last (d) dimension must be 1.  Base pointers must be 16-byte aligned
- *    and each (b, h, t) stride a multiple of 16 bytes.
+ *    and each (b, h, t) stride a multiple of 16 bytes.  The t stride may
+ *    not exceed SAF_MAX_T_STRIDE elements (SAF_EUNSUPPORTED otherwise).
  *  - a and r are fp32 [H][prior_len] (row stride prior_len, prior_len >= T);
  *    rows of ordinary heads are never read.  Only entries [0, T) of a row are
  *    used, which is exact: causal rows never reach further.
@@ -73,6 +74,7 @@ extern "C" {
 /* Limits. */
 #define SAF_MAX_HEADS 256
 #define SAF_MAX_T (1 << 20)
+#define SAF_MAX_T_STRIDE (1 << 24) /* elements between consecutive rows */
 
 /*
  * Shape, layout and head-state description of one call.

@@ -110,6 +110,10 @@ def test_fwd_rejects_bad_pointers_and_strides(b):
     assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1  # lse null
     p.q_stride = b._i64x3(0, 0, 12)  # t stride not a multiple of 16 bytes
     assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == -1
+    p.q_stride = b._i64x3(0, 0, (1 << 24) + 8)  # t stride beyond SAF_MAX_T_STRIDE
+    assert call(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE) == -2
+    p.q_stride = b._i64x3(0, 0, 1 << 24)  # largest accepted t stride: the v tensor fails next
+    assert call(FAKE, FAKE, FAKE + 2, FAKE, FAKE, FAKE, FAKE) == -1
     p2, arr2 = _params(b, frozen=[1, 1, 1, 1])  # all frozen: q/k unused, a/r required
     st = b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p2), None, None, FAKE, None, FAKE, FAKE, FAKE, None, 0, None)
     assert st == -1
