@@ -161,25 +161,27 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
   const int qt0 = k0 / kKvBM;  // < nqt since k0 < T
   const int nqt = (T + kKvBM - 1) / kKvBM;
 
-  // Next-tile operands are loaded into registers at the start of a tile and
-  // written to LDS at its end.
-  TileStage<D, kKvBM, kThreads> qst, ost;
+  // Next-tile operands are requested at the start of a tile (Q and dO copied
+  // straight into the idle LDS buffer, lse and delta into registers) and
+  // completed at its end.
+  TileDma<D, kKvBM> qdma, odma;
+  qdma.init(A.q.st);
+  odma.init(A.dout.st);
   ScalarStage lsv, dlv;
-  auto load_next = [&](int i0) {
-    qst.load(qg, A.q.st, i0, T);
-    ost.load(dog, A.dout.st, i0, T);
+  auto load_next = [&](int i0, int buf) {
+    qdma.issue(qg, A.q.st, i0, T, smem + buf * C::TILE);
+    odma.issue(dog, A.dout.st, i0, T, smem + (2 + buf) * C::TILE);
     lsv.load(lse, i0, T);
     dlv.load(dl, i0, T);
   };
   auto store_next = [&](int buf) {
-    qst.store(smem + buf * C::TILE);
-    ost.store(smem + (2 + buf) * C::TILE);
     if (threadIdx.x < kKvBM) {
       fb[buf * kKvBM + threadIdx.x] = lsv.valid ? lsv.v * kLog2e : __builtin_inff();  // padding: P = 0
       fb[(2 + buf) * kKvBM + threadIdx.x] = dlv.valid ? -dlv.v : 0.f;
     }
+    wait_vm_loads();
   };
-  load_next(qt0 * kKvBM);
+  load_next(qt0 * kKvBM, 0);
   store_next(0);
   __syncthreads();
 
@@ -198,7 +200,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
-    if (more) load_next(i0 + kKvBM);
+    if (more) load_next(i0 + kKvBM, bi ^ 1);
     const lds_bf16* Q = smem + bi * C::TILE;
     const lds_bf16* O = smem + (2 + bi) * C::TILE;
     const lds_f32* ls = fb + bi * kKvBM;
@@ -289,37 +291,34 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
 
-  TileStage<D, kKvBM, kThreads> ost[G];
-  auto load_do = [&](int i0) {
+  TileDma<D, kKvBM> odma;
+  odma.init(A.dout.st);
+  auto load_do = [&](int i0, int buf) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
       const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
-      ost[gb].load(g, A.dout.st, i0, T);
+      odma.issue(g, A.dout.st, i0, T, smem + (buf * G + gb) * C::TILE);
     }
-  };
-  auto store_do = [&](int buf) {
-#pragma unroll
-    for (int gb = 0; gb < G; ++gb) ost[gb].store(smem + (buf * G + gb) * C::TILE);
   };
   // Next-tile operands: dO tiles, z2 = log N (log2 units) of the tile rows,
   // and the r band over offsets [i0 - k0 - (BN-1), i0 + BM - 1 - k0]; loaded
   // into registers at the start of a tile, written to LDS at its end.
   ScalarStage zv;
   BandStage<C::BAND, kThreads> band;
-  auto load_next = [&](int i0) {
-    load_do(i0);
+  auto load_next = [&](int i0, int buf) {
+    load_do(i0, buf);
     zv.load(lse, i0, T);
     band.load(rrow, i0 - k0 - (kKvBN - 1), T);
   };
   auto store_next = [&](int buf) {
-    store_do(buf);
     lds_f32* zs = fb + buf * FSTRIDE;
     if (threadIdx.x < kKvBM) zs[threadIdx.x] = zv.valid ? zv.v * kLog2e : __builtin_inff();
     band.store(zs + kKvBM);
+    wait_vm_loads();
   };
 
-  load_next(qt0 * kKvBM);  // qt0 < nqt since k0 < T
+  load_next(qt0 * kKvBM, 0);  // qt0 < nqt since k0 < T
   store_next(0);
   __syncthreads();
 
@@ -333,7 +332,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
     const bool more = (qt + 1) < nqt;
-    if (more) load_next(i0 + kKvBM);
+    if (more) load_next(i0 + kKvBM, bi ^ 1);
     const lds_f32* zs = fb + bi * FSTRIDE;
     const lds_f32* rs = zs + kKvBM;
     if (i0 + kKvBM - 1 >= wk_lo) {
@@ -374,7 +373,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
 // Key-block pass for every head in one launch: program p -> (key block, slot),
 // key block 0 (the most queries) first; the slot's list selects the body.
 template <int D>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 2 : 1)) void bwd_kv_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_kv_kernel(BwdArgs A) {
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_k = n_ord_prog + A.n_frz * A.n_groups;
@@ -432,11 +431,14 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   const int last_key = min(q0 + kQBM, T) - 1;
   const int ntiles = last_key / kQBN + 1;
 
-  TileStage<D, kQBN, kThreads> kst, vst;
-  kst.load(kg, A.k.st, 0, T);
-  vst.load(vg, A.v.st, 0, T);
-  kst.store(smem);
-  vst.store(smem + 2 * C::TILE);
+  // K and V tiles are copied straight into the idle LDS buffer at the start
+  // of the previous tile.
+  TileDma<D, kQBN> kdma, vdma;
+  kdma.init(A.k.st);
+  vdma.init(A.v.st);
+  kdma.issue(kg, A.k.st, 0, T, smem);
+  vdma.issue(vg, A.v.st, 0, T, smem + 2 * C::TILE);
+  wait_vm_loads();
   __syncthreads();
 
   f32x16 dqa[C::NDB];
@@ -450,8 +452,8 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
     const int j0 = t * kQBN;
     const bool more = (t + 1) < ntiles;
     if (more) {
-      kst.load(kg, A.k.st, j0 + kQBN, T);
-      vst.load(vg, A.v.st, j0 + kQBN, T);
+      kdma.issue(kg, A.k.st, j0 + kQBN, T, smem + ((t + 1) & 1) * C::TILE);
+      vdma.issue(vg, A.v.st, j0 + kQBN, T, smem + (2 + ((t + 1) & 1)) * C::TILE);
     }
     const lds_bf16* K = smem + (t & 1) * C::TILE;
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
@@ -488,8 +490,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
       }
     }
     if (more) {
-      kst.store(smem + ((t + 1) & 1) * C::TILE);
-      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE);
+      wait_vm_loads();
     }
     __syncthreads();
   };

@@ -100,11 +100,14 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
-  TileStage<D, kBN, kThreads> kst, vst;
-  kst.load(kg, A.k.st, 0, T);
-  vst.load(vg, A.v.st, 0, T);
-  kst.store(smem);
-  vst.store(smem + 2 * C::TILE);
+  // K and V tiles are copied straight into the idle LDS buffer at the start
+  // of the previous tile.
+  TileDma<D, kBN> kdma, vdma;
+  kdma.init(A.k.st);
+  vdma.init(A.v.st);
+  kdma.issue(kg, A.k.st, 0, T, smem);
+  vdma.issue(vg, A.v.st, 0, T, smem + 2 * C::TILE);
+  wait_vm_loads();
   __syncthreads();
 
   f32x16 oacc[C::NDB];
@@ -121,8 +124,8 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
     if (more) {
-      kst.load(kg, A.k.st, j0 + kBN, T);
-      vst.load(vg, A.v.st, j0 + kBN, T);
+      kdma.issue(kg, A.k.st, j0 + kBN, T, smem + ((t + 1) & 1) * C::TILE);
+      vdma.issue(vg, A.v.st, j0 + kBN, T, smem + (2 + ((t + 1) & 1)) * C::TILE);
     }
     const lds_bf16* K = smem + (t & 1) * C::TILE;
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
@@ -187,8 +190,7 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
       }
     }
     if (more) {
-      kst.store(smem + ((t + 1) & 1) * C::TILE);
-      vst.store(smem + (2 + ((t + 1) & 1)) * C::TILE);
+      wait_vm_loads();
     }
     __syncthreads();
   };
@@ -262,28 +264,28 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   // written to LDS at its end: the V tiles of the group, a (log2 units) of
   // the tile keys (-inf for keys >= T) and the r band over the offsets of the
   // tile, band[x] = r2[q0 - j0 - (BN-1) + x].
-  TileStage<D, kBN, kThreads> vst[G];
+  TileDma<D, kBN> vdma;
+  vdma.init(A.v.st);
   ScalarStage av;
   BandStage<C::BAND, kThreads> band;
-  auto load_next = [&](int j0) {
+  auto load_next = [&](int j0, int buf) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
       const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
-      vst[gb].load(vg, A.v.st, j0, T);
+      vdma.issue(vg, A.v.st, j0, T, smem + (buf * G + gb) * C::TILE);
     }
     av.load(arow, j0, T);
     band.load(rrow, q0 - j0 - (kBN - 1), T);
   };
   auto store_next = [&](int buf) {
-#pragma unroll
-    for (int gb = 0; gb < G; ++gb) vst[gb].store(smem + (buf * G + gb) * C::TILE);
     lds_f32* as = fbase + buf * FSTRIDE;
     if (threadIdx.x < kBN) as[threadIdx.x] = av.valid ? av.v * kLog2e : kNegInf;
     band.store(as + kBN);
+    wait_vm_loads();
   };
 
-  load_next(0);
+  load_next(0, 0);
   store_next(0);
   __syncthreads();
 
@@ -296,7 +298,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
-    if (more) load_next(j0 + kBN);
+    if (more) load_next(j0 + kBN, (t & 1) ^ 1);
     const int buf = t & 1;
     const lds_f32* as = fbase + buf * FSTRIDE;
     const lds_f32* rs = as + kBN;

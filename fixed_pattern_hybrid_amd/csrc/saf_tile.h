@@ -100,4 +100,76 @@ struct BandStage {
   }
 };
 
+// A [ROWS][D] bf16 tile copied from global memory straight into LDS (buffer
+// loads with the LDS modifier; no registers, no LDS store instructions), in
+// the padded LdsLayout<D> arrangement.  One wave-wide load writes 64
+// consecutive 16-byte granules of LDS (lane l at granule l); a padded row is
+// D/8 + 1 granules, so lane l of load m fetches granule g = 64 m + l, i.e.
+// row g / (D/8 + 1), chunk g % (D/8 + 1); the pad granule and rows >= T take
+// an offset outside the buffer range and are written as zeros.  The four
+// waves of the block share the loads (wave w issues loads w, w+4, ...).
+// The data is visible to the block after s_waitcnt vmcnt(0) in every wave
+// and a barrier.
+template <int D, int ROWS>
+struct TileDma {
+  static constexpr int NG = D / 8 + 1;       // granules per padded row
+  static constexpr int NI = ROWS * NG / 64;  // wave-wide loads per tile
+  static constexpr int PER = (NI + 3) / 4;   // loads per wave (4 waves)
+  static constexpr int kOob = 0x7ffffff0;    // beyond any buffer range used here
+  static_assert(ROWS * NG % 64 == 0, "tile must be whole wave-wide loads");
+  static_assert(LdsLayout<D>::PITCH * 2 == NG * 16, "padded row is D/8 + 1 granules");
+  int off[PER];
+  int ste;
+
+  // st: row stride of the tensor (elements, at most SAF_MAX_T_STRIDE)
+  __device__ __forceinline__ void init(int64_t st) {
+    ste = (int)(st > D ? st : D);  // a one-row tensor may have any stride
+    const int l = lane_id();
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int m = w + 4 * k;
+      const int g = 64 * m + l;
+      const int row = g / NG, col = g - row * NG;
+      off[k] = (m >= NI || col == NG - 1) ? kOob : row * ste * 2 + col * 16;
+    }
+  }
+
+  // Copy rows row0 .. row0+ROWS-1 of `base` into `tile` (zeros from row T).
+  // The loads are issued from inline assembly, which the compiler's wait
+  // insertion does not see: otherwise it would wait for them before the
+  // first LDS read of the tile being computed (it cannot tell the two
+  // buffers apart).  Completion is awaited explicitly (wait_vm_loads); waits
+  // the compiler places for its own loads stay correct, as they only become
+  // stricter.  The buffer must not be read before that wait and a barrier.
+  __device__ __forceinline__ void issue(const __bf16* base, int64_t st, int row0, int T,
+                                        lds_bf16* tile) const {
+    const int rows = T - row0 < ROWS ? T - row0 : ROWS;
+    const int nrec = rows >= 1 ? (int)((int64_t)(rows - 1) * ste * 2 + D * 2) : 0;
+    const uint64_t addr = (uint64_t)(base + (int64_t)row0 * st);
+    // raw buffer resource: 48-bit base, stride 0, byte range, data format
+    const u32x4 rsrc = {(unsigned)addr, (unsigned)(addr >> 32) & 0xffffu, (unsigned)nrec,
+                        (unsigned)kBufferFlags};
+    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    const unsigned lds0 = (unsigned)(uintptr_t)tile;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int m = w + 4 * k;
+      if (m < NI) {
+        asm volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "buffer_load_dwordx4 %0, %2, 0 offen lds"
+            :
+            : "v"(off[k]), "s"(lds0 + 1024u * m), "s"(rsrc)
+            : "memory", "m0");
+      }
+    }
+  }
+};
+
+// Wait until this wave's outstanding vector-memory loads (including loads
+// into LDS) have completed.
+__device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
 }  // namespace saf
