@@ -525,7 +525,9 @@ hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
   const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::kv_lds, stream, args);
+  // only the program kinds present need room (less LDS, more blocks per CU)
+  const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? C::kv_lds : C::kv_frz_lds) : C::kv_ord_lds;
+  hipLaunchKernelGGL(bwd_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), need, stream, args);
   return hipGetLastError();
 }
 

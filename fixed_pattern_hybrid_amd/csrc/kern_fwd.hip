@@ -372,7 +372,9 @@ hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
   args.nqb = (args.T + kBM - 1) / kBM;
   const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nqb;
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(kThreads), lds, stream, args);
+  // only the program kinds present need room (less LDS, more blocks per CU)
+  const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? lds : C::frz_lds) : C::ord_lds;
+  hipLaunchKernelGGL(fwd_kernel<D>, dim3((unsigned)grid), dim3(kThreads), need, stream, args);
   return hipGetLastError();
 }
 
