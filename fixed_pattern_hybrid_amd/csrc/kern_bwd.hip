@@ -41,7 +41,8 @@ struct BwdCfg {
   static constexpr int TILE = 64 * PITCH;
   static constexpr int BAND = kKvBM + kKvBN;  // r band of a (query tile, key block)
   // per buffer: z2[kKvBM], then 4 copies of the band, copy c shifted by c
-  static constexpr int FSTRIDE = kKvBM + 4 * BAND;
+  static constexpr int BSTRIDE = band_stride(BAND);  // distance between band copies
+  static constexpr int FSTRIDE = kKvBM + 4 * BSTRIDE;
   // key-block pass, ordinary: Q and dO tiles (double-buffered) + lse2 and delta
   static constexpr size_t kv_ord_lds = size_t(2) * 2 * TILE * 2 + size_t(2) * 2 * kKvBM * 4;
   // key-block pass, frozen: G dO tiles (double-buffered) + z2 and the r band
@@ -341,7 +342,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
       // and (base + xj) mod 4 = xj mod 4 is fixed per lane.
       const int xj = (kKvBN - 1) - (j - k0);
       const int cpy = xj & 3;
-      const lds_f32* rc = rs + cpy * C::BAND - cpy;
+      const lds_f32* rc = rs + cpy * C::BSTRIDE - cpy;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float wv[8];

@@ -41,7 +41,8 @@ struct FwdCfg {
   static constexpr int TILE = kBN * PITCH;     // elements of one staged tile
   static constexpr int BAND = kBM + kBN;       // r band length (BM + BN - 1, padded)
   // per buffer: a2[kBN], then 4 copies of the band, copy c shifted by c
-  static constexpr int FSTRIDE = kBN + 4 * BAND;
+  static constexpr int BSTRIDE = band_stride(BAND);  // distance between band copies
+  static constexpr int FSTRIDE = kBN + 4 * BSTRIDE;
   static constexpr size_t ord_lds = size_t(2) * 2 * TILE * 2;
   static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4;
 };
@@ -131,55 +132,72 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
     if (!MASK || j0 <= wq_hi) {
       f32x16 s[2];
+      auto scores = [&]() {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        s[c] = f32x16{};
+        for (int c = 0; c < 2; ++c) {
+          s[c] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks)
-          s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
-      }
-      if constexpr (MASK) {
+          for (int ks = 0; ks < C::NKS; ++ks)
+            s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
+        }
+        if constexpr (MASK) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int j = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
+              if (j > i) s[c][r] = kNegInf;
+            }
+        }
+      };
+      // p = exp2(s * scale_log2 - m) in place; returns this lane's sum
+      auto exps = [&](float m) {
+        float psum = 0.f;
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int j = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (j > i) s[c][r] = kNegInf;
+            const float p = fast_exp2(fmaf(s[c][r], sl2, -m));
+            s[c][r] = p;
+            psum += p;
           }
-      }
-      float mx = kNegInf;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
-      mx = fmaxf(mx, xor32(mx));
-      // Lazy rescaling: the reference maximum only moves when the tile's
-      // maximum exceeds it by more than 8 (log2 units), so p <= 2^8 and the
-      // accumulator rescale is skipped on most tiles.  The final O = acc / l
-      // and lse = m + log2(l) are exact for any reference value.
-      const float mt = mx * sl2;
-      const bool grow = mt > m_run + 8.f;
-      const float m_new = grow ? mt : m_run;
-      const float alpha = fast_exp2(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[c][r], sl2, -m_new));
-          s[c][r] = p;
-          psum += p;
-        }
-      l_run = fmaf(l_run, alpha, psum);
-      m_run = m_new;
-      if (__any(grow)) {
+        return psum;
+      };
+      scores();
+      // Lazy rescaling: the reference maximum m_run only moves when a score
+      // exceeds it by more than 8 (log2 units), so every p <= 2^8.  The
+      // exponentials are first taken against m_run; a lane sum <= 2^8 proves
+      // every p <= 2^8 (and finite), and then the tile maximum is never
+      // needed.  Otherwise (the first tile, a grown maximum, or a rare false
+      // alarm) the scores are recomputed and the maximum is taken as usual.
+      // The final O = acc / l and lse = m + log2(l) are exact for any
+      // reference value.
+      float psum = exps(m_run);
+      if (__any(!(psum <= 256.f))) {
         // keep this a real branch (it is taken on few tiles)
         asm volatile("");
+        scores();
+        float mx = kNegInf;
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+        mx = fmaxf(mx, xor32(mx));
+        const float mt = mx * sl2;
+        const bool grow = mt > m_run + 8.f;
+        const float m_new = grow ? mt : m_run;
+        const float alpha = fast_exp2(m_run - m_new);
+        psum = exps(m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        if (__any(grow)) {
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        }
       }
+      l_run += psum;
       // O^T += V^T P^T
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
@@ -308,7 +326,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
       // y0 = xi - base - 3, and y0 mod 4 = (xi + 1) mod 4 is fixed per lane.
       const int xi = (i - q0) + kBN - 1;
       const int cpy = (xi + 1) & 3;
-      const lds_f32* rc = rs + cpy * C::BAND - cpy;  // rc[y] = band[y] for y = 0 mod 4 reads
+      const lds_f32* rc = rs + cpy * C::BSTRIDE - cpy;  // rc[y] = band[y] for y = 0 mod 4 reads
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float wv[8];

@@ -70,14 +70,25 @@ struct ScalarStage {
   }
 };
 
+// Distance in floats between the four copies of a band: the smallest value
+// >= BAND that is 16 (mod 64).  A wave reads the copies with 16-byte loads
+// whose copy index follows the lane's position mod 4; with copies 4 granules
+// apart in bank order (64 banks of 4 bytes), 16 consecutive lanes touch each
+// bank at most twice (copies a multiple of 64 floats apart share banks:
+// 4-way conflicts).
+constexpr int band_stride(int band) { return (band + 47) / 64 * 64 + 16; }
+
 // The relative-position band of a frozen tile, band[x] = log2(e) * r[dmin + x]
 // for x in [0, BAND) (-inf where dmin + x falls outside [0, T)), stored in LDS
-// as four copies: copy c holds band[y + c] at y (-inf past the band's end), so
-// that aligned 16-byte reads fetch four consecutive offsets in any phase.
-// Thread x loads band[x] once and writes it into every copy that holds it.
+// as four copies STRIDE floats apart: copy c holds band[y + c] at y (-inf past
+// the band's end), so that aligned 16-byte reads fetch four consecutive
+// offsets in any phase.  Thread x loads band[x] once and writes it into every
+// copy that holds it.
 template <int BAND, int NTHR>
 struct BandStage {
+  static constexpr int STRIDE = band_stride(BAND);
   static_assert(BAND + 3 <= NTHR, "one band entry per thread");
+  static_assert(STRIDE >= BAND && STRIDE % 4 == 0, "copies keep 16-byte alignment");
   float v;
   bool valid;
   __device__ __forceinline__ void load(const float* rrow, int dmin, int T) {
@@ -94,7 +105,7 @@ struct BandStage {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int y = x - c;
-        if (y >= 0 && y < BAND) rs[c * BAND + y] = val;
+        if (y >= 0 && y < BAND) rs[c * STRIDE + y] = val;
       }
     }
   }
