@@ -393,7 +393,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_kv_kernel(Bwd
 // Query-block pass, ordinary head (b, h, qb): dQ = s dS K.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdArgs A) {
   using C = BwdCfg<D>;
   SAF_DYN_LDS(smem);
   const int per_q = A.B * A.n_ord;
@@ -428,6 +428,10 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
   const int64_t rowv = ((int64_t)b * A.H + h) * T + i;
   const float l2 = (i < T) ? A.lse[rowv] * kLog2e : __builtin_inff();
   const float dl = (i < T) ? A.delta[rowv] : 0.f;
+  // dP accumulators start at -delta, so the products yield dP - delta directly
+  f32x16 ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
 
   const int last_key = min(q0 + kQBM, T) - 1;
   const int ntiles = last_key / kQBN + 1;
@@ -463,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         s[c] = f32x16{};
-        dp[c] = f32x16{};
+        dp[c] = ndl;
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
@@ -479,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void bwd_q_kernel(BwdArgs A) {
             const int jj = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
             if (jj > i) p = 0.f;
           }
-          dp[c][r] = p * (dp[c][r] - dl);
+          dp[c][r] = p * dp[c][r];
         }
       // dQ^T += K^T dS^T
 #pragma unroll
