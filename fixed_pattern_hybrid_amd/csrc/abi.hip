@@ -87,13 +87,12 @@ size_t bwd_ws_bytes(const saf_attn_params* p) {
   return round_up((size_t)p->B * p->H * p->T * sizeof(float), 256);
 }
 
-int lognorm_chunks(int T) { return (T + saf::kLognormChunk - 1) / saf::kLognormChunk; }
-
-// bf16 forward with frozen heads: per-chunk normaliser partials, one float2
-// per (frozen head, key chunk, row).  The fp32 forward needs none.
+// bf16 forward with frozen heads: normaliser partials, one float2 per
+// (frozen head, key group, row), at most 32 groups.  The fp32 forward needs
+// none.
 size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
   if (p->dtype != SAF_BF16 || n_frz == 0) return 0;
-  return round_up((size_t)n_frz * lognorm_chunks(p->T) * p->T * 2 * sizeof(float), 256);
+  return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
 }
 
 // Records stage event k when the caller asked for it.
@@ -197,8 +196,9 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
     if (p->dtype == SAF_BF16) {
       // partials only; the forward's frozen programs merge them and write lse
       args.lz_part = static_cast<const float2*>(ws);
-      args.n_chunks = lognorm_chunks(p->T);
-      if (saf::launch_lognorm_partial(la, static_cast<float2*>(ws), stream) != hipSuccess)
+      args.lz_group = saf::lognorm_group_keys(p->T);
+      args.lz_ngroups = saf::lognorm_groups(p->T);
+      if (saf::launch_lognorm_partial(la, static_cast<float2*>(ws), args.lz_group, stream) != hipSuccess)
         return SAF_EHIP;
     } else {
       if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;

@@ -255,8 +255,8 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   float z2 = 0.f;
   if (i < T) {
     float M = kNegInf, S = 0.f;
-    const float2* part = A.lz_part + (int64_t)hidx * A.n_chunks * T + i;
-    const int cmax = i / kLognormChunk;  // chunks 0..cmax hold this row's terms
+    const float2* part = A.lz_part + (int64_t)hidx * A.lz_ngroups * T + i;
+    const int cmax = i / A.lz_group;  // groups 0..cmax hold this row's terms
     for (int c0 = 0; c0 <= cmax; c0 += 4) {
       float2 p[4];
 #pragma unroll

@@ -2,7 +2,7 @@
 // ("When Can Attention Heads Be Statically Defined?", Section 3.2,
 // Equation 3: N(i) = sum_{k<=i} exp(a[k] + r[i-k])).
 //
-// Normalisers are computed over chunks of 1024 keys.  One block handles 64
+// Normalisers are computed over chunks of 256 keys.  One block handles 64
 // rows; each of its four waves takes every fourth key of a row, and the four
 // partial sums are merged at the end.  Within a (row block, key chunk) the
 // terms factor as
@@ -16,10 +16,11 @@
 //
 //   lognorm_kernel          one block per (head, row block), all chunks in
 //                           turn; writes log N (natural log).
-//   lognorm_partial_kernel  one block per (head, row block, chunk); writes
-//                           the chunk's (max, sum) pair per row, merged later
-//                           by the forward's frozen programs.  This spreads
-//                           the triangular work over many more blocks.
+//   lognorm_partial_kernel  one block per (head, row block, key group of one
+//                           or more chunks); writes the group's (max, sum)
+//                           pair per row, merged later by the forward's
+//                           frozen programs.  This spreads the triangular
+//                           work over many more blocks.
 #include "saf_internal.h"
 #include "saf_device.h"
 
@@ -160,24 +161,31 @@ __global__ __launch_bounds__(kNT) void lognorm_kernel(LognormArgs A, int identit
   }
 }
 
-// Grid: (row blocks, chunks, listed heads).  Writes float2 (max, sum) at
-// part[(hidx * nchunks + chunk) * T + i] for rows i >= chunk start.
-__global__ __launch_bounds__(kNT) void lognorm_partial_kernel(LognormArgs A, float2* part) {
+// Grid: (row blocks, key groups, listed heads); group g covers keys
+// [g * group_keys, (g + 1) * group_keys), processed kTK keys at a time.
+// Writes float2 (max, sum) at part[(hidx * ngroups + g) * T + i] for the rows
+// i >= the group's first key.
+__global__ __launch_bounds__(kNT) void lognorm_partial_kernel(LognormArgs A, float2* part, int group_keys) {
   __shared__ ChunkSmem sm;
   const int hidx = blockIdx.z;
   const int h = A.heads[hidx];
   const int T = A.T;
   const int i0 = blockIdx.x * kRows;
-  const int k0 = blockIdx.y * kTK;
+  const int kb = blockIdx.y * group_keys;
   const int last_row = min(i0 + kRows, T) - 1;
-  if (k0 > last_row) return;  // no row of this block reaches the chunk (whole block)
+  if (kb > last_row) return;  // no row of this block reaches the group (whole block)
+  const int kend = min(kb + group_keys, last_row + 1);
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
-  float cm, cs;
-  chunk_partial(arow, rrow, T, i0, k0, sm, cm, cs);
+  float M = kNegInf, S = 0.f;
+  for (int k0 = kb; k0 < kend; k0 += kTK) {
+    float cm, cs;
+    chunk_partial(arow, rrow, T, i0, k0, sm, cm, cs);
+    lse_merge(M, S, cm, cs);
+  }
   const int i = i0 + lane_id();
-  if (wave_id() == 0 && i < T && k0 <= i)
-    part[((int64_t)hidx * gridDim.y + blockIdx.y) * T + i] = make_float2(cm, cs);
+  if (wave_id() == 0 && i < T && kb <= i)
+    part[((int64_t)hidx * gridDim.y + blockIdx.y) * T + i] = make_float2(M, S);
 }
 
 // Dense eager pattern of one head: row i per block, exact max-shifted sum.
@@ -230,10 +238,12 @@ hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream) 
   return hipGetLastError();
 }
 
-hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, hipStream_t stream) {
+hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, int group_keys,
+                                  hipStream_t stream) {
   if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
-  dim3 grid((args.T + kRows - 1) / kRows, (args.T + kTK - 1) / kTK, args.n_heads);
-  hipLaunchKernelGGL(lognorm_partial_kernel, grid, dim3(kNT), 0, stream, args, part);
+  if (group_keys <= 0 || group_keys % kTK != 0) return hipErrorInvalidValue;
+  dim3 grid((args.T + kRows - 1) / kRows, (args.T + group_keys - 1) / group_keys, args.n_heads);
+  hipLaunchKernelGGL(lognorm_partial_kernel, grid, dim3(kNT), 0, stream, args, part, group_keys);
   return hipGetLastError();
 }
 

@@ -8,7 +8,20 @@
 namespace saf {
 
 constexpr int kMaxHeads = 256;
-constexpr int kLognormChunk = 1024;  // keys per normaliser partial
+constexpr int kLognormChunk = 256;     // keys per step of a normaliser block
+constexpr int kLognormMaxGroups = 32;  // at most this many partials per row
+
+// Keys per normaliser partial: a multiple of kLognormChunk chosen so that a
+// row has at most kLognormMaxGroups partials (bounding the workspace).
+inline int lognorm_group_keys(int T) {
+  const int per = (T + kLognormMaxGroups - 1) / kLognormMaxGroups;
+  const int rounded = (per + kLognormChunk - 1) / kLognormChunk * kLognormChunk;
+  return rounded > kLognormChunk ? rounded : kLognormChunk;
+}
+inline int lognorm_groups(int T) {
+  const int g = lognorm_group_keys(T);
+  return (T + g - 1) / g;
+}
 
 // One strided [B][H][T][D] tensor: base pointer and element strides of
 // (b, h, t); the d stride is 1.
@@ -29,10 +42,11 @@ struct FwdArgs {
   int frz_group;     // batch elements per frozen program
   int n_groups;      // ceil(B / frz_group)
   int nqb;           // number of query blocks
-  // bf16 path: per-chunk normaliser partials (max, sum) in log2 units,
-  // [n_frz][n_chunks][T]; the frozen programs merge them and write lse.
+  // bf16 path: normaliser partials (max, sum) in log2 units over groups of
+  // lz_group keys, [n_frz][lz_ngroups][T]; the frozen programs merge them
+  // and write lse.
   const float2* lz_part;
-  int n_chunks;
+  int lz_group, lz_ngroups;
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
 };
@@ -71,7 +85,7 @@ struct LognormArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream);
-hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, hipStream_t stream);
+hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, int group_keys, hipStream_t stream);
 hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const float* r, float* w,
                                 hipStream_t stream);
 

@@ -167,13 +167,18 @@ struct TileDma {
     for (int k = 0; k < PER; ++k) {
       const int m = w + 4 * k;
       if (m < NI) {
+        // M0 holds the LDS destination; its previous value is restored so
+        // that the statement has no effect on registers the compiler owns.
+        unsigned saved;
         asm volatile(
-            "s_mov_b32 m0, %1\n\t"
+            "s_mov_b32 %0, m0\n\t"
+            "s_mov_b32 m0, %2\n\t"
             "s_nop 0\n\t"
-            "buffer_load_dwordx4 %0, %2, 0 offen lds"
-            :
+            "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
+            "s_mov_b32 m0, %0"
+            : "=&s"(saved)
             : "v"(off[k]), "s"(lds0 + 1024u * m), "s"(rsrc)
-            : "memory", "m0");
+            : "memory");
       }
     }
   }

@@ -112,9 +112,11 @@ typedef struct saf_attn_params {
  *   lse     : device fp32 [B][H][T] output (see conventions above).
  *   ws      : workspace of at least saf_hybrid_attn_workspace_bytes(p, 0)
  *             bytes, 256-byte aligned (may be NULL when that is 0).  bf16
- *             with frozen heads needs n_frozen * ceil(T / 1024) * T * 8
- *             bytes (rounded up to 256) for per-key-chunk partial sums of
- *             the row normalisers; fp32, or no frozen head, needs none.
+ *             with frozen heads needs n_frozen * G * T * 8 bytes (rounded
+ *             up to 256) for partial sums of the row normalisers over G key
+ *             groups, G = ceil(T / K) with K the smallest multiple of 256
+ *             that is >= T / 32 (so G <= 32); fp32, or no frozen head,
+ *             needs none.
  *             Contents on entry are ignored and left undefined on return.
  * Kernels: the frozen heads' row normalisers (bf16: chunk partials, merged
  * by the frozen programs of the next launch), then one mixed-head launch.

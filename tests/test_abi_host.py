@@ -136,10 +136,13 @@ def test_bwd_workspace_checks(b):
 
 
 def test_fwd_workspace_checks(b):
-    T = 2100  # three key chunks of 1024
+    T = 2100  # nine key groups of 256
     p, arr = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1])
     need = b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0)
-    assert need == -(-(2 * 3 * T * 8) // 256) * 256
+    assert need == -(-(2 * 9 * T * 8) // 256) * 256
+    for T2, groups in ((256, 1), (257, 2), (8192, 32), (8193, 17), (32768, 32), (1 << 20, 32)):
+        p2, arr2 = _params(b, B=1, H=4, T=T2, frozen=[0, 1, 0, 1])
+        assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p2), 0) == -(-(2 * groups * T2 * 8) // 256) * 256
     args = [FAKE] * 7
     assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, None, need, None) == -3
     assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE, need - 1, None) == -3
