@@ -254,7 +254,10 @@ def main():
     has_frz = any(fz)
     has_ord = not all(fz)
     names_f = (["lognorm"] if has_frz else []) + ["fwd"]
-    names_b = ["bwd_pre", "bwd_kv"] + (["bwd_q"] if has_ord else [])
+    if cfg.dtype == "bf16":
+        names_b = (["bwd_q"] if has_ord else []) + ["bwd_kv"]
+    else:
+        names_b = ["bwd_pre", "bwd_kv"] + (["bwd_q"] if has_ord else [])
     n_fwd_ev = len(names_f) + 1
     n_bwd_ev = len(names_b) + 1
     stream = torch.cuda.current_stream()

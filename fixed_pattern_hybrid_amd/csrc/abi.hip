@@ -265,15 +265,14 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   if (stg.mark() != hipSuccess) return SAF_EHIP;
   hipError_t e;
   if (p->dtype == SAF_BF16) {
-    // delta + zero frozen dQ/dK, key-block passes, query-block pass
-    e = saf::launch_bwd_pre_bf16(args, p->D, stream);
-    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
-    e = saf::launch_bwd_kv_bf16(args, p->D, stream);
-    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    // query-block pass (also stores delta), then the mixed key-block pass
+    // (which reads delta and writes the frozen heads' zero dQ/dK rows)
     if (n_ord > 0) {
       e = saf::launch_bwd_q_bf16(args, p->D, stream);
       if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
     }
+    e = saf::launch_bwd_kv_bf16(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
   } else {
     e = saf::launch_bwd_pre_f32(args, p->D, stream);
     if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;

@@ -10,14 +10,17 @@
 // dS = P o (dP - delta), delta_i = sum_d dO[i][d] * O[i][d],
 // dV = P^T dO, dK = s dS^T Q, dQ = s dS K.
 //
-// Kernels:
-//   bwd_pre : delta for ordinary heads; +0.0 into frozen heads' dQ, dK.
+// Kernels (in launch order):
+//   bwd_q   : one program per (b, h, 128-query block) of ordinary heads; keys
+//             in tiles of 64; accumulator dQ^T.  It also computes
+//             delta = rowsum(dO * O) for its rows (each lane already holds
+//             half of its row of dO) and stores it for the next pass.
 //   bwd_kv  : one launch; one program per (b, h, 128-key block) for ordinary
 //             heads and per (h, 128-key block, batch group) for frozen heads;
-//             queries in tiles of 64.  Accumulators are dV^T and dK^T so that each
-//             lane owns one key and the C registers of S feed the products.
-//   bwd_q   : one program per (b, h, 128-query block) of ordinary heads;
-//             keys in tiles of 64; accumulator dQ^T.
+//             queries in tiles of 64.  Accumulators are dV^T and dK^T so that
+//             each lane owns one key and the C registers of S feed the
+//             products.  Frozen programs also write the +0.0 rows of dQ and
+//             dK for their keys.
 #include <type_traits>
 
 #include "saf_internal.h"
@@ -73,53 +76,6 @@ __device__ __forceinline__ void store_rows_t(const TensorRef& o, int b, int h, i
 
 __device__ __forceinline__ float bf16lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
 __device__ __forceinline__ float bf16hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
-
-// ---------------------------------------------------------------------------
-// delta = rowsum(dO * O) (ordinary heads); zero dQ, dK (frozen heads).
-// Grid: (ceil(T/32), B*H); eight lanes per row, each taking 16-byte chunks
-// c, c+8, ... of the row, so a wave reads eight whole rows contiguously.
-// ---------------------------------------------------------------------------
-constexpr int kPreLPR = 8;                // lanes per row
-constexpr int kPreRows = 256 / kPreLPR;  // rows per block
-
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs A) {
-  constexpr int NCH = D / 8;  // 16-byte chunks per row
-  const int bh = blockIdx.y;
-  const int b = bh / A.H, h = bh - b * A.H;
-  const int sub = threadIdx.x % kPreLPR;
-  const int i = blockIdx.x * kPreRows + threadIdx.x / kPreLPR;
-  const bool live = i < A.T;  // every lane of a row group shares it
-  if (A.is_frozen[h]) {
-    if (!live) return;
-    __bf16* dq = (__bf16*)A.dq.ptr + (int64_t)b * A.dq.sb + (int64_t)h * A.dq.sh + (int64_t)i * A.dq.st;
-    __bf16* dk = (__bf16*)A.dk.ptr + (int64_t)b * A.dk.sb + (int64_t)h * A.dk.sh + (int64_t)i * A.dk.st;
-#pragma unroll
-    for (int c = sub; c < NCH; c += kPreLPR) {
-      sstore16(dq + 8 * c, u32x4{0u, 0u, 0u, 0u});
-      sstore16(dk + 8 * c, u32x4{0u, 0u, 0u, 0u});
-    }
-    return;
-  }
-  float acc = 0.f;
-  if (live) {
-    const __bf16* o = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
-    const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh + (int64_t)i * A.dout.st;
-#pragma unroll
-    for (int c = sub; c < NCH; c += kPreLPR) {
-      const u32x4 x = gload16(o + 8 * c), y = gload16(g + 8 * c);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf16lo(x[e]), bf16lo(y[e]), acc);
-        acc = fmaf(bf16hi(x[e]), bf16hi(y[e]), acc);
-      }
-    }
-  }
-  // row groups are aligned 8-lane groups of the wave
-#pragma unroll
-  for (int m = 1; m < kPreLPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-  if (live && sub == 0) A.delta[((int64_t)b * A.H + h) * A.T + i] = acc;
-}
 
 // ---------------------------------------------------------------------------
 // Key-block pass, ordinary head (b, h, kb).
@@ -282,6 +238,23 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
   const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
+
+  // frozen heads have no query/key path: dQ and dK rows are exactly +0.0
+  if (j < T && hl == 0) {
+#pragma unroll
+    for (int gb = 0; gb < G; ++gb) {
+      if (gb < nb) {
+        const int b = b0 + gb;
+        __bf16* dq = (__bf16*)A.dq.ptr + (int64_t)b * A.dq.sb + (int64_t)h * A.dq.sh + (int64_t)j * A.dq.st;
+        __bf16* dk = (__bf16*)A.dk.ptr + (int64_t)b * A.dk.sb + (int64_t)h * A.dk.sh + (int64_t)j * A.dk.st;
+#pragma unroll
+        for (int c = 0; c < D / 8; ++c) {
+          sstore16(dq + 8 * c, u32x4{0u, 0u, 0u, 0u});
+          sstore16(dk + 8 * c, u32x4{0u, 0u, 0u, 0u});
+        }
+      }
+    }
+  }
   const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, same for every b
 
   // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and 4 shifted copies
@@ -425,9 +398,22 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
       of[ks] = qf[ks];
     }
   }
+  // delta_i = sum_d dO[i][d] O[i][d]: this lane holds half of the row (the
+  // other half is in lane l ^ 32); stored for the key-block pass.
   const int64_t rowv = ((int64_t)b * A.H + h) * T + i;
   const float l2 = (i < T) ? A.lse[rowv] * kLog2e : __builtin_inff();
-  const float dl = (i < T) ? A.delta[rowv] : 0.f;
+  float dl = 0.f;
+  if (i < T) {
+    const __bf16* og = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, gload16(og + 16 * ks + 8 * hl));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = fmaf((float)of[ks][e], (float)ov[e], dl);
+    }
+  }
+  dl += xor32(dl);
+  if (hl == 0 && i < T) A.delta[rowv] = dl;
   // dP accumulators start at -delta, so the products yield dP - delta directly
   f32x16 ndl;
 #pragma unroll
@@ -506,13 +492,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   store_rows_t<D>(A.dq, b, h, i, T, dqa, A.scale);
 }
 
-template <int D>
-hipError_t launch_pre_d(const BwdArgs& args, hipStream_t stream) {
-  dim3 grid((args.T + kPreRows - 1) / kPreRows, args.B * args.H);
-  hipLaunchKernelGGL(bwd_pre_kernel<D>, grid, dim3(256), 0, stream, args);
-  return hipGetLastError();
-}
-
 template <typename K>
 hipError_t set_lds(K kernel, size_t bytes) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -550,15 +529,6 @@ hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream) {
-  switch (D) {
-    case 64: return launch_pre_d<64>(args, stream);
-    case 96: return launch_pre_d<96>(args, stream);
-    case 128: return launch_pre_d<128>(args, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
 
 hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream) {
   switch (D) {

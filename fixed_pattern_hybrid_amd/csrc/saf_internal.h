@@ -93,7 +93,6 @@ hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
 
 // bf16 path: one mixed-head launch for the forward and for the key-block pass.
 hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream);
-hipError_t launch_bwd_pre_bf16(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream);
 
