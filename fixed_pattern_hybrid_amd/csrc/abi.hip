@@ -5,6 +5,7 @@
 #include "saf_internal.h"
 
 #include <cmath>
+#include <climits>
 #include <cstring>
 
 namespace {
@@ -51,6 +52,12 @@ int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   *n_frz = f;
   // every (b, h, t) offset and B*H*T must fit comfortably in int64 / grids
   if ((int64_t)p->B * p->H * p->T > (int64_t)1 << 40) return SAF_EUNSUPPORTED;
+  if (p->dtype == SAF_BF16) {
+    // one-dimensional grids of at most B * H * ceil(T / 128) programs
+    if ((int64_t)p->B * p->H * ((p->T + 127) / 128) > INT32_MAX) return SAF_EUNSUPPORTED;
+  } else if ((int64_t)p->B * p->H > 65535) {
+    return SAF_EUNSUPPORTED;  // fp32 kernels put (b, h) in the grid's second dimension
+  }
   return SAF_OK;
 }
 

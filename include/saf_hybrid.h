@@ -75,6 +75,9 @@ extern "C" {
 #define SAF_MAX_HEADS 256
 #define SAF_MAX_T (1 << 20)
 #define SAF_MAX_T_STRIDE (1 << 24) /* elements between consecutive rows */
+/* Also rejected with SAF_EUNSUPPORTED: B * H * T > 2^40; for bf16,
+ * B * H * ceil(T / 128) > 2^31 - 1 (programs per launch); for fp32,
+ * B * H > 65535. */
 
 /*
  * Shape, layout and head-state description of one call.

@@ -135,6 +135,20 @@ def test_bwd_workspace_checks(b):
     assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(bad), 1) == 0
 
 
+def test_grid_size_limits(b):
+    args = [FAKE] * 7
+    # bf16: B*H*T within 2^40 but B*H*ceil(T/128) programs beyond 2^31 - 1
+    p, arr = _params(b, B=65535, H=256, T=32768, prior_len=32768)
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, None, 0, None) == -2
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 1) == 0
+    # fp32: B*H beyond the 65535 limit of the grid's second dimension
+    p2, arr2 = _params(b, B=300, H=256, T=16, dtype=b.SAF_F32)
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p2), *args, None, 0, None) == -2
+    # just inside both limits: rejected only later, on the fake pointers' alignment
+    p3, arr3 = _params(b, B=255, H=256, T=16, dtype=b.SAF_F32)
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p3), FAKE + 2, *args[1:], None, 0, None) == -1
+
+
 def test_fwd_workspace_checks(b):
     T = 2100  # nine key groups of 256
     p, arr = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1])

@@ -128,7 +128,15 @@ def test_head_dims_and_masks(B, D, mask):
     run_full_parity(B, cfg)
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("H,T", [(40, 100), (256, 24)])
+def test_many_heads(B, H, T):
+    # head lists up to the maximum head count; every third head frozen
+    cfg = CONFIGS["pages_check_t129"].with_(H=H, T=T, B=3, prior_len=None, frozen=tuple(range(1, H, 3)),
+                                            name=f"heads{H}")
+    run_full_parity(B, cfg)
+
+
+@pytest.mark.parametrize("D", [16, 32, 64, 96, 128])
 def test_fp32_path(B, D):
     cfg = CONFIGS["tiny"].with_(D=D, T=70, B=2, H=3, frozen=(2,), name=f"fp32_D{D}")
     run_full_parity(B, cfg)
