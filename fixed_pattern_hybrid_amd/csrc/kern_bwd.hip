@@ -41,6 +41,7 @@ struct BwdCfg {
   static constexpr int NDB = D / 32;
   static constexpr int NKS = D / 16;
   static constexpr int G = 2;
+  static constexpr int CG = D == 64 ? 2 : 1;  // key-block pass: 32-query halves computed together
   static constexpr int TILE = 64 * PITCH;
   static constexpr int BAND = kKvBM + kKvBN;  // r band of a (query tile, key block)
   // per buffer: z2[kKvBM], then 4 copies of the band, copy c shifted by c
@@ -121,7 +122,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
   // Next-tile operands are requested at the start of a tile (Q and dO copied
   // straight into the idle LDS buffer, lse and delta into registers) and
   // completed at its end.
-  TileDma<D, kKvBM> qdma, odma;
+  TileDma<D, kKvBM, (D == 64)> qdma, odma;
   qdma.init(A.q.st);
   odma.init(A.dout.st);
   ScalarStage lsv, dlv;
@@ -163,49 +164,57 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     const lds_f32* ls = fb + bi * kKvBM;
     const lds_f32* nd = fb + (2 + bi) * kKvBM;
     if (!MASK || i0 + kKvBM - 1 >= wk_lo) {
-      // S = Q K^T and dP - delta = dO V^T - delta (accumulator seeded with -delta)
-      f32x16 s[2], dp[2];
+      // The tile's two 32-query halves are processed together (d = 64) or
+      // one after the other (larger d, which halves the live S and dP
+      // registers so that two waves fit per SIMD).
+      constexpr int CG = C::CG;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        s[c] = f32x16{};
+      for (int c0 = 0; c0 < 2; c0 += CG) {
+        // S = Q K^T and dP - delta = dO V^T - delta (accumulator seeded with -delta)
+        f32x16 s[CG], dp[CG];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 d4 = lds_read_f4(nd + 32 * c + 8 * q4 + 4 * hl);
+        for (int cc = 0; cc < CG; ++cc) {
+          const int c = c0 + cc;
+          s[cc] = f32x16{};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dp[c][4 * q4 + e] = d4[e];
-        }
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const f32x4 d4 = lds_read_f4(nd + 32 * c + 8 * q4 + 4 * hl);
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          s[c] = mfma32(lds_frag_nat<D>(Q, 32 * c, 16 * ks), kf[ks], s[c]);
-          dp[c] = mfma32(lds_frag_nat<D>(O, 32 * c, 16 * ks), vf[ks], dp[c]);
-        }
-      }
+            for (int e = 0; e < 4; ++e) dp[cc][4 * q4 + e] = d4[e];
+          }
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int ib = 32 * c + 8 * q4 + 4 * hl;  // first of 4 consecutive tile rows
-          const f32x4 l4 = lds_read_f4(ls + ib);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * q4 + e;
-            float p = fast_exp2(fmaf(s[c][r], sl2, -l4[e]));
-            if constexpr (MASK) {
-              if ((i0 + ib + e) < j) p = 0.f;
-            }
-            s[c][r] = p;
-            dp[c][r] = p * dp[c][r];
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            s[cc] = mfma32(lds_frag_nat<D>(Q, 32 * c, 16 * ks), kf[ks], s[cc]);
+            dp[cc] = mfma32(lds_frag_nat<D>(O, 32 * c, 16 * ks), vf[ks], dp[cc]);
           }
         }
-      // dV^T += dO^T P ; dK^T += Q^T dS
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 pf = pack_acc8(s[st >> 1], 8 * (st & 1));
-        const bf16x8 sf = pack_acc8(dp[st >> 1], 8 * (st & 1));
+        for (int cc = 0; cc < CG; ++cc)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          dva[db] = mfma32(lds_frag_tr<D>(O, 16 * st, 32 * db), pf, dva[db]);
-          dka[db] = mfma32(lds_frag_tr<D>(Q, 16 * st, 32 * db), sf, dka[db]);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int ib = 32 * (c0 + cc) + 8 * q4 + 4 * hl;  // first of 4 consecutive tile rows
+            const f32x4 l4 = lds_read_f4(ls + ib);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * q4 + e;
+              float p = fast_exp2(fmaf(s[cc][r], sl2, -l4[e]));
+              if constexpr (MASK) {
+                if ((i0 + ib + e) < j) p = 0.f;
+              }
+              s[cc][r] = p;
+              dp[cc][r] = p * dp[cc][r];
+            }
+          }
+        // dV^T += dO^T P ; dK^T += Q^T dS
+#pragma unroll
+        for (int st = 2 * c0; st < 2 * (c0 + CG); ++st) {
+          const bf16x8 pf = pack_acc8(s[(st >> 1) - c0], 8 * (st & 1));
+          const bf16x8 sf = pack_acc8(dp[(st >> 1) - c0], 8 * (st & 1));
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) {
+            dva[db] = mfma32(lds_frag_tr<D>(O, 16 * st, 32 * db), pf, dva[db]);
+            dka[db] = mfma32(lds_frag_tr<D>(Q, 16 * st, 32 * db), sf, dka[db]);
+          }
         }
       }
     }
@@ -265,7 +274,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
 
-  TileDma<D, kKvBM> odma;
+  TileDma<D, kKvBM, (D == 64)> odma;
   odma.init(A.dout.st);
   auto load_do = [&](int i0, int buf) {
 #pragma unroll
@@ -347,7 +356,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
 // Key-block pass for every head in one launch: program p -> (key block, slot),
 // key block 0 (the most queries) first; the slot's list selects the body.
 template <int D>
-__global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_kv_kernel(BwdArgs A) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 2)) void bwd_kv_kernel(BwdArgs A) {
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_k = n_ord_prog + A.n_frz * A.n_groups;

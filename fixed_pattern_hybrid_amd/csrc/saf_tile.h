@@ -121,7 +121,7 @@ struct BandStage {
 // waves of the block share the loads (wave w issues loads w, w+4, ...).
 // The data is visible to the block after s_waitcnt vmcnt(0) in every wave
 // and a barrier.
-template <int D, int ROWS>
+template <int D, int ROWS, bool KEEP = true>
 struct TileDma {
   static constexpr int NG = D / 8 + 1;       // granules per padded row
   static constexpr int NI = ROWS * NG / 64;  // wave-wide loads per tile
@@ -129,20 +129,25 @@ struct TileDma {
   static constexpr int kOob = 0x7ffffff0;    // beyond any buffer range used here
   static_assert(ROWS * NG % 64 == 0, "tile must be whole wave-wide loads");
   static_assert(LdsLayout<D>::PITCH * 2 == NG * 16, "padded row is D/8 + 1 granules");
-  int off[PER];
+  // Per-lane byte offsets of this wave's loads: kept in registers (KEEP) or
+  // recomputed at each issue where registers are scarcer.
+  static constexpr bool kKeep = KEEP;
+  int off[kKeep ? PER : 1];
   int ste;
+
+  __device__ __forceinline__ int offset(int k) const {
+    const int m = __builtin_amdgcn_readfirstlane(wave_id()) + 4 * k;
+    const int g = 64 * m + lane_id();
+    const int row = g / NG, col = g - row * NG;
+    return (m >= NI || col == NG - 1) ? kOob : row * ste * 2 + col * 16;
+  }
 
   // st: row stride of the tensor (elements, at most SAF_MAX_T_STRIDE)
   __device__ __forceinline__ void init(int64_t st) {
     ste = (int)(st > D ? st : D);  // a one-row tensor may have any stride
-    const int l = lane_id();
-    const int w = __builtin_amdgcn_readfirstlane(wave_id());
+    if constexpr (kKeep) {
 #pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int m = w + 4 * k;
-      const int g = 64 * m + l;
-      const int row = g / NG, col = g - row * NG;
-      off[k] = (m >= NI || col == NG - 1) ? kOob : row * ste * 2 + col * 16;
+      for (int k = 0; k < PER; ++k) off[k] = offset(k);
     }
   }
 
@@ -177,7 +182,7 @@ struct TileDma {
             "buffer_load_dwordx4 %1, %3, 0 offen lds\n\t"
             "s_mov_b32 m0, %0"
             : "=&s"(saved)
-            : "v"(off[k]), "s"(lds0 + 1024u * m), "s"(rsrc)
+            : "v"(kKeep ? off[kKeep ? k : 0] : offset(k)), "s"(lds0 + 1024u * m), "s"(rsrc)
             : "memory");
       }
     }
