@@ -23,21 +23,27 @@
 //                           work over many more blocks.
 #include "saf_internal.h"
 #include "saf_device.h"
+#include "saf_tile.h"
 
 namespace saf {
 namespace {
 
 constexpr int kRows = 64;   // rows per block (one per lane of each wave)
-constexpr int kLanes = 4;   // key lanes: wave w takes keys w, w+4, w+8, ...
+constexpr int kLanes = 4;   // key lanes: wave w takes the chunk's key groups 4w..4w+3, 4w+16.., ...
 constexpr int kTK = kLognormChunk;  // keys per chunk
 constexpr int kBand = kRows + kTK;
 constexpr int kNT = kRows * kLanes;
+constexpr int kBS = band_stride(kBand);  // distance between the copies of exp2(r2 - mr)
+static_assert(kTK % 16 == 0 && kBand + 3 <= 2 * kNT, "chunk layout");
 
 struct ChunkSmem {
   float a2s[kTK];    // a (log2 units) of the chunk
   float r2s[kBand];  // r (log2 units) of the chunk's band
-  float eas[kTK];    // exp2(a2 - ma)
-  float ers[kBand];  // exp2(r2 - mr)
+  __attribute__((aligned(16))) float eas[kTK];  // exp2(a2 - ma)
+  // exp2(r2 - mr) in four copies: copy c holds band entry y + c at y (0
+  // past the end), so four consecutive entries starting anywhere are one
+  // aligned 16-byte read
+  __attribute__((aligned(16))) float ers[4 * kBS];
   float red[8];
   float cm[kLanes][kRows];
   float cs[kLanes][kRows];
@@ -95,36 +101,61 @@ __device__ void chunk_partial(const float* arow, const float* rrow, int T, int i
   if (ma == kNegInf) ma = 0.f;
   if (mr == kNegInf) mr = 0.f;
   for (int x = threadIdx.x; x < kTK; x += kNT) sm.eas[x] = fast_exp2(sm.a2s[x] - ma);
-  for (int x = threadIdx.x; x < kBand; x += kNT) sm.ers[x] = fast_exp2(sm.r2s[x] - mr);
+  for (int x = threadIdx.x; x < kBand + 3; x += kNT) {
+    const float e = x < kBand ? fast_exp2(sm.r2s[x] - mr) : 0.f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int y = x - c;
+      if (y >= 0 && y < kBand) sm.ers[c * kBS + y] = e;
+    }
+  }
   __syncthreads();
 
+  // This wave's keys: groups of four, x = 4 * (kl + 4u), up to the last key
+  // any row of the block reaches (later keys of a row have band offset < 0,
+  // whose exp2(r2 - mr) is 0, and keys >= T have exp2(a2 - ma) = 0, so every
+  // lane may run the same loop).  Interleaving the groups over the waves
+  // balances the diagonal chunk, where rows reach only its first keys.
+  const int xq = 4 * __builtin_amdgcn_readfirstlane(kl);
+  const int xlast = min(min(i0 + kRows, T) - 1 - k0, kTK - 1);
   float M = kNegInf, S = 0.f;
-  if (i < T && k0 + kl <= i) {
-    const int kend = min(kTK - 1, i - k0);  // last chunk-local key of this row
-    const int xb = i - k0 - dmin;           // band index of offset i - k0
+  if (xq <= xlast) {
+    const int xb = i - k0 - dmin;  // band index of offset i - k0 (key 0 of the chunk)
     float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-    int x = kl;
-    for (; x + 3 * kLanes <= kend; x += 4 * kLanes) {
-      s0 = fmaf(sm.eas[x], sm.ers[xb - x], s0);
-      s1 = fmaf(sm.eas[x + kLanes], sm.ers[xb - x - kLanes], s1);
-      s2 = fmaf(sm.eas[x + 2 * kLanes], sm.ers[xb - x - 2 * kLanes], s2);
-      s3 = fmaf(sm.eas[x + 3 * kLanes], sm.ers[xb - x - 3 * kLanes], s3);
+    // keys x..x+3 need band entries xb-x-3 .. xb-x (reversed); y0 mod 4 is
+    // the same for every x (a multiple of 4), which picks the copy
+    const int cpy = (xb + 1) & 3;  // = (xb - x - 3) mod 4
+    const lds_f32* rc = (const lds_f32*)sm.ers + cpy * kBS - cpy;
+    const lds_f32* ea = (const lds_f32*)sm.eas;
+#pragma unroll 4
+    for (int x = xq; x <= xlast; x += 4 * kLanes) {
+      const f32x4 e4 = lds_read_f4(ea + x);
+      const f32x4 r4 = lds_read_f4(rc + (xb - x - 3));
+      s0 = fmaf(e4[0], r4[3], s0);
+      s1 = fmaf(e4[1], r4[2], s1);
+      s2 = fmaf(e4[2], r4[1], s2);
+      s3 = fmaf(e4[3], r4[0], s3);
     }
-    for (; x <= kend; x += kLanes) s0 = fmaf(sm.eas[x], sm.ers[xb - x], s0);
     const float s = (s0 + s1) + (s2 + s3);
-    if (s >= 0x1p-20f) {
-      M = ma + mr;
-      S = s;
-    } else {
-      // exact fallback: max-shifted sum of this lane's terms in the chunk
-      float cm = kNegInf;
-      for (int y = kl; y <= kend; y += kLanes) cm = fmaxf(cm, sm.a2s[y] + sm.r2s[xb - y]);
-      float cs = 0.f;
-      if (cm != kNegInf)
-        for (int y = kl; y <= kend; y += kLanes) cs += fast_exp2(sm.a2s[y] + sm.r2s[xb - y] - cm);
-      if (cs > 0.f) {
-        M = cm;
-        S = cs;
+    if (i < T) {
+      if (s >= 0x1p-20f) {
+        M = ma + mr;
+        S = s;
+      } else {
+        // exact fallback: max-shifted sum of this lane's terms in the chunk
+        // (this wave's groups of four keys)
+        const int kend = min(xlast, i - k0);
+        float cm = kNegInf;
+        for (int g = xq; g <= kend; g += 4 * kLanes)
+          for (int y = g; y < g + 4 && y <= kend; ++y) cm = fmaxf(cm, sm.a2s[y] + sm.r2s[xb - y]);
+        float cs = 0.f;
+        if (cm != kNegInf)
+          for (int g = xq; g <= kend; g += 4 * kLanes)
+            for (int y = g; y < g + 4 && y <= kend; ++y) cs += fast_exp2(sm.a2s[y] + sm.r2s[xb - y] - cm);
+        if (cs > 0.f) {
+          M = cm;
+          S = cs;
+        }
       }
     }
   }
