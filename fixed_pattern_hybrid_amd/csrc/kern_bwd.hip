@@ -232,16 +232,19 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
 // ---------------------------------------------------------------------------
 // Key-block pass, frozen head (h, kb, batch group): dV = W^T dO.
 // ---------------------------------------------------------------------------
-template <int D>
+// NG: batch elements this program covers (the group size, or 1 for a
+// final group of one, which would otherwise repeat its element).
+template <int D, int NG>
 __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int kb, lds_bf16* smem) {
   using C = BwdCfg<D>;
-  constexpr int G = C::G;
+  constexpr int G = NG;      // batch elements computed
+  constexpr int GL = C::G;   // batch slots of the LDS layout
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
   const int j = k0 + 32 * w + (l & 31);
   const int wk_lo = k0 + 32 * w;
-  const int b0 = grp * G;
+  const int b0 = grp * GL;  // groups are GL batch elements apart
   const int nb = min(G, A.B - b0);
 
   const float* arow = A.a + (int64_t)h * A.prior_len;
@@ -268,7 +271,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
 
   // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and 4 shifted copies
   // of the r band (copy c holds band[y + c] at y)
-  lds_f32* fb = (lds_f32*)(smem + 2 * G * C::TILE);
+  lds_f32* fb = (lds_f32*)(smem + 2 * GL * C::TILE);
   constexpr int FSTRIDE = C::FSTRIDE;
 
   const int qt0 = k0 / kKvBM;
@@ -281,7 +284,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
       const __bf16* g = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
-      odma.issue(g, A.dout.st, i0, T, smem + (buf * G + gb) * C::TILE);
+      odma.issue(g, A.dout.st, i0, T, smem + (buf * GL + gb) * C::TILE);
     }
   };
   // Next-tile operands: dO tiles, z2 = log N (log2 units) of the tile rows,
@@ -341,7 +344,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            dva[gb][db] = mfma32(lds_frag_tr<D>(smem + (bi * G + gb) * C::TILE, 16 * st, 32 * db),
+            dva[gb][db] = mfma32(lds_frag_tr<D>(smem + (bi * GL + gb) * C::TILE, 16 * st, 32 * db),
                                  wf, dva[gb][db]);
       }
     }
@@ -367,7 +370,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 2)) void bwd_kv_kernel(Bwd
     kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], kb, smem);
   } else {
     const int f = rem - n_ord_prog;
-    kv_frozen<D>(A, A.frz_heads[f / A.n_groups], f % A.n_groups, kb, smem);
+    const int h = A.frz_heads[f / A.n_groups], grp = f % A.n_groups;
+    if (A.B - grp * BwdCfg<D>::G >= BwdCfg<D>::G) kv_frozen<D, BwdCfg<D>::G>(A, h, grp, kb, smem);
+    else kv_frozen<D, 1>(A, h, grp, kb, smem);
   }
 }
 

@@ -228,23 +228,26 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
 // Frozen head program (h, query block, batch group):
 // W[i][j] = exp(a[j] + r[i-j] - log N(i)), rebuilt per tile.
 // ---------------------------------------------------------------------------
-template <int D>
+// NG: batch elements this program covers (the group size, or 1 for a
+// final group of one, which would otherwise repeat its element).
+template <int D, int NG>
 __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, int qb, lds_bf16* smem) {
   using C = FwdCfg<D>;
-  constexpr int G = C::G;
+  constexpr int G = NG;      // batch elements computed
+  constexpr int GL = C::G;   // batch slots of the LDS layout
 
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int q0 = qb * kBM;
   const int i = q0 + 32 * w + (l & 31);
   const int wq_hi = q0 + 32 * w + 31;
-  const int b0 = grp * G;
+  const int b0 = grp * GL;  // groups are GL batch elements apart
   const int nb = min(G, A.B - b0);
 
   // LDS: V tiles [buf][gb], then per buffer a2[kBN] and 4 shifted copies of
   // the r band (copy c holds band[y + c] at y), so that each lane reads the
   // four offsets of four consecutive keys with one aligned 16-byte read.
-  lds_f32* fbase = (lds_f32*)(smem + 2 * G * C::TILE);
+  lds_f32* fbase = (lds_f32*)(smem + 2 * GL * C::TILE);
   constexpr int FSTRIDE = C::FSTRIDE;
 
   const int h = A.frz_heads[hidx];
@@ -291,7 +294,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
       const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
-      vdma.issue(vg, A.v.st, j0, T, smem + (buf * G + gb) * C::TILE);
+      vdma.issue(vg, A.v.st, j0, T, smem + (buf * GL + gb) * C::TILE);
     }
     av.load(arow, j0, T);
     band.load(rrow, q0 - j0 - (kBN - 1), T);
@@ -343,7 +346,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
         for (int gb = 0; gb < G; ++gb)
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db)
-            oacc[gb][db] = mfma32(lds_frag_tr<D>(smem + (buf * G + gb) * C::TILE, 16 * st, 32 * db),
+            oacc[gb][db] = mfma32(lds_frag_tr<D>(smem + (buf * GL + gb) * C::TILE, 16 * st, 32 * db),
                                   wf, oacc[gb][db]);
       }
     }
@@ -373,7 +376,9 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs A) {
     fwd_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], qb, smem);
   } else {
     const int f = rem - n_ord_prog;
-    fwd_frozen<D>(A, f / A.n_groups, f % A.n_groups, qb, smem);
+    const int hidx = f / A.n_groups, grp = f % A.n_groups;
+    if (A.B - grp * FwdCfg<D>::G >= FwdCfg<D>::G) fwd_frozen<D, FwdCfg<D>::G>(A, hidx, grp, qb, smem);
+    else fwd_frozen<D, 1>(A, hidx, grp, qb, smem);
   }
 }
 

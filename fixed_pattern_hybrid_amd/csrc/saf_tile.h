@@ -163,9 +163,12 @@ struct TileDma {
     const int rows = T - row0 < ROWS ? T - row0 : ROWS;
     const int nrec = rows >= 1 ? (int)((int64_t)(rows - 1) * ste * 2 + D * 2) : 0;
     const uint64_t addr = (uint64_t)(base + (int64_t)row0 * st);
-    // raw buffer resource: 48-bit base, stride 0, byte range, data format
-    const u32x4 rsrc = {(unsigned)addr, (unsigned)(addr >> 32) & 0xffffu, (unsigned)nrec,
-                        (unsigned)kBufferFlags};
+    // raw buffer resource: 48-bit base, stride 0, byte range, data format.
+    // Every input is the same across the block; readfirstlane makes that
+    // explicit so that the descriptor is formed in scalar registers.
+    const u32x4 rsrc = {(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)addr),
+                        (unsigned)__builtin_amdgcn_readfirstlane((int)((unsigned)(addr >> 32) & 0xffffu)),
+                        (unsigned)__builtin_amdgcn_readfirstlane(nrec), (unsigned)kBufferFlags};
     const int w = __builtin_amdgcn_readfirstlane(wave_id());
     const unsigned lds0 = (unsigned)(uintptr_t)tile;
 #pragma unroll
