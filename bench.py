@@ -53,6 +53,7 @@ def flops(cfg, n_ord=None, n_frz=None, B=None):
     return f
 
 
+DEFAULT_CONFIG = "gpt2_124m_4k_25pct"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_kv_gpt2-124m-layer_B8_T4096_d64_25pct.txt")
 KERNEL_SOURCES = ("kern_bwd.hip", "saf_device.h", "saf_tile.h", "saf_internal.h")
 
@@ -214,7 +215,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="gpt2_124m_4k_25pct")
+    ap.add_argument("--config", default=DEFAULT_CONFIG,
+                    help="workload (synth.CONFIGS key); the default is the headline metric's; others: "
+                         "gpt2_124m_4k_50pct_interleaved, 1b_8k_rank_share, prefill_32k, pages_check_t129, tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-per-head", action="store_true")
@@ -316,8 +319,11 @@ def main():
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
                 "kernel_ms": round(kern_ms[dom], 4)}
+    metric = ("hybrid-attn fwd+bwd TFLOP/s & MFMA util, 124M/4K shape, 25% heads frozen"
+              if args.config == DEFAULT_CONFIG else
+              f"hybrid-attn {'fwd+bwd' if do is not None else 'fwd'} TFLOP/s, workload {cfg.name}")
     out = {
-        "metric": "hybrid-attn fwd+bwd TFLOP/s & MFMA util, 124M/4K shape, 25% heads frozen",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
