@@ -253,7 +253,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   const int h = A.frz_heads[hidx];
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
-  // log N(i) in log2 units: merge the per-chunk partials of this row, and
+  // log N(i) in log2 units: merge the key-group partials of this row, and
   // record it as the row's lse for every batch element of the group.
   float z2 = 0.f;
   if (i < T) {

@@ -142,7 +142,6 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 __device__ __forceinline__ void sstore16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
-__device__ __forceinline__ void lds_store16(lds_bf16* p, u32x4 v) { *(lds_u32x4*)p = v; }
 __device__ __forceinline__ f32x4 lds_read_f4(const lds_f32* p) { return *(const lds_f32x4*)p; }
 
 }  // namespace saf

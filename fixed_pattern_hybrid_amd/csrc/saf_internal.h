@@ -106,6 +106,5 @@ hipError_t launch_bwd_q_f32(const BwdArgs& args, int D, hipStream_t stream);
 constexpr int kFwdBM = 128;     // queries per forward program
 constexpr int kBwdKvBN = 128;   // keys per key-block program
 constexpr int kBwdQBM = 128;    // queries per query-block program
-constexpr int kFrzGroup = 4;    // batch elements sharing one rebuilt pattern tile
 
 }  // namespace saf

@@ -1,4 +1,6 @@
-// Cooperative global -> register -> LDS staging of bf16 row tiles.
+// Staging from global memory into LDS: bf16 row tiles copied straight into
+// LDS by the block's waves, and per-row values and relative-position bands
+// that pass through registers.
 #pragma once
 
 #include "saf_device.h"
@@ -8,54 +10,6 @@ namespace saf {
 // Word 3 of a raw (unformatted, unswizzled) buffer resource on gfx9-family
 // parts: 32-bit data format, so dword loads return the stored bits.
 constexpr int kBufferFlags = 0x00020000;
-
-// A [ROWS][D] bf16 tile of a strided tensor (rows row0 .., row stride `st`
-// elements, unit stride along D), staged by NTHR threads in 16-byte chunks:
-// loaded into registers at the start of a tile, stored to LDS at its end.
-//
-// The loads go through a buffer resource whose range ends after the last
-// row below T: chunks of rows >= T fall outside it and read as zero without
-// touching memory, so the loads carry no branches, clamps or selects, and the
-// 32-bit offsets are fixed per thread.  Nothing consumes a loaded register
-// before the store, so the compute of the tile overlaps the loads.
-// Offsets are row * st * 2 bytes (row < ROWS), which the host keeps below
-// 2^31 by bounding st.
-template <int D, int ROWS, int NTHR>
-struct TileStage {
-  static constexpr int CPR = D / 8;  // 16-byte chunks per row
-  static constexpr int CHUNKS = ROWS * CPR;
-  static constexpr int PER = (CHUNKS + NTHR - 1) / NTHR;
-  static_assert(CHUNKS % NTHR == 0, "tile must split evenly over the threads");
-  u32x4 buf[PER];
-
-  __device__ __forceinline__ void load(const __bf16* base, int64_t st, int row0, int T) {
-    // Rows of one head never overlap when T > 1 (st >= D); a one-row tensor
-    // may have any stride, and its missing rows use the stride D so that
-    // they still fall outside the range.
-    const int64_t ste = st > D ? st : D;
-    const int rows = T - row0 < ROWS ? T - row0 : ROWS;
-    const int nrec = rows >= 1 ? (int)((int64_t)(rows - 1) * ste * 2 + D * 2) : 0;
-    const __amdgpu_buffer_rsrc_t rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)row0 * st), (short)0, nrec, kBufferFlags);
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = threadIdx.x + p * NTHR;
-      const int row = idx / CPR, ch = idx % CPR;
-      buf[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rsrc, row * (int)ste * 2 + ch * 16, 0, 0));
-    }
-  }
-
-  // store into a tile with the LdsLayout<D> arrangement
-  __device__ __forceinline__ void store(lds_bf16* lds) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = threadIdx.x + p * NTHR;
-      const int row = idx / CPR, ch = idx % CPR;
-      lds_store16(lds + LdsLayout<D>::off(row, ch * 8), buf[p]);
-    }
-  }
-};
 
 // One float per thread from src[i0 + threadIdx.x], prefetched into a register
 // at the start of a tile and written to LDS at its end.  Out-of-range rows
