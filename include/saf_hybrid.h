@@ -48,6 +48,11 @@
  *    inside a kernel surface at the caller's next synchronisation.
  *  - The library has no mutable global state; concurrent calls on different
  *    streams are safe.  Results are bitwise deterministic (no atomics).
+ *  - Calls may be recorded by stream capture into a HIP graph: they enqueue
+ *    kernel launches only (plus event records when stage events are asked
+ *    for), allocate nothing and issue no memset.  Make one call with the
+ *    same head dimension and dtype outside capture first: it sets each
+ *    kernel's LDS size attribute once per process.
  */
 #ifndef SAF_HYBRID_H
 #define SAF_HYBRID_H

@@ -177,6 +177,52 @@ def test_stage_events_do_not_change_results(B):
     assert evs[0].elapsed_time(evs[2]) >= 0.0
 
 
+def test_graph_capture_replays_match_eager(B):
+    # The entry points allocate nothing and issue no memsets, so a caller can
+    # capture forward + backward into a HIP graph; every replay (with eager
+    # work and synchronisation between replays) must equal the eager result.
+    cfg = CONFIGS["pages_check_t129"].with_(B=3, T=300, prior_len=None, name="graph")
+    inp = make_inputs(cfg, with_do=True)
+    dev = upload(inp)
+    q, k, v, do, a, r = dev["q"], dev["k"], dev["v"], dev["do"], dev["a"], dev["r"]
+    fz = [int(x) for x in inp.frozen]
+    O0, L0 = B.saf_hybrid_attn_fwd(q, k, v, fz, a, r)
+    G0 = B.saf_hybrid_attn_bwd(q, k, v, O0, do, L0, fz, a, r)
+    torch.cuda.synchronize()
+
+    O, L = torch.empty_like(O0), torch.empty_like(L0)
+    dq, dk, dv = (torch.empty_like(x) for x in G0)
+    prm = B.Params(v, fz, a.shape[1])
+    wsf = torch.empty(max(B.workspace_bytes(prm, False), 256), dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device="cuda")
+
+    def step():
+        B.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=O, lse=L, workspace=wsf)
+        B.saf_hybrid_attn_bwd(q, k, v, O, do, L, fz, a, r, dq=dq, dk=dk, dv=dv, workspace=wsb)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (O, L, dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(O, O0) and torch.equal(L, L0)
+        for got, ref in zip((dq, dk, dv), G0):
+            assert torch.equal(got, ref)
+        B.saf_hybrid_attn_fwd(q, k, v, fz, a, r)  # eager work between replays
+        torch.cuda.synchronize()
+
+
 # --------------------------------------------------------------------------
 # Pattern entry points
 # --------------------------------------------------------------------------
