@@ -134,6 +134,46 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise ValueError(f"unsupported dtype {t.dtype}")
 
 
+def _check_like(name: str, t, ref: torch.Tensor, shape=None, dtype=None) -> None:
+    """t must match ref's device and the given (default: ref's) shape and dtype.
+
+    The library sees only pointers and strides, so a smaller or differently
+    typed tensor would be read or written past its end; this is where that
+    is caught.
+    """
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    want_shape = tuple(ref.shape) if shape is None else tuple(shape)
+    want_dtype = ref.dtype if dtype is None else dtype
+    if tuple(t.shape) != want_shape:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want_shape}")
+    if t.dtype != want_dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {want_dtype}")
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+
+
+def _check_layer_inputs(v: torch.Tensor, a: torch.Tensor, r: torch.Tensor, **tensors) -> None:
+    if v.dim() != 4:
+        raise ValueError("v must be [B, H, T, D]")
+    _dtype_code(v)
+    H = v.shape[1]
+    if a.dim() != 2 or a.shape[0] != H:
+        raise ValueError("a and r must both be [H, Tp]")
+    _check_like("r", r, a)
+    if a.dtype != torch.float32 or not a.is_contiguous() or not r.is_contiguous():
+        raise ValueError("a and r must be contiguous float32 [H, Tp]")
+    if a.device != v.device:
+        raise ValueError("a and r must be on the device of v")
+    for name, t in tensors.items():
+        _check_like(name, t, v)
+
+
+def _require_gpu(v: torch.Tensor) -> None:
+    if not v.is_cuda:
+        raise ValueError("tensors must be on a GPU")
+
+
 def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -146,9 +186,9 @@ class Params:
     def __init__(self, v: torch.Tensor, frozen: Sequence[int], prior_len: int,
                  softmax_scale: Optional[float] = None, events=None):
         B, H, T, D = v.shape
-        self.frozen_arr = (ctypes.c_uint8 * H)(*[int(x) for x in frozen])
         if len(frozen) != H:
             raise ValueError("frozen mask needs one entry per head")
+        self.frozen_arr = (ctypes.c_uint8 * H)(*[int(x) for x in frozen])
         self.p = SafParams()
         self.p.struct_bytes = ctypes.sizeof(SafParams)
         self.p.B, self.p.H, self.p.T, self.p.D = B, H, T, D
@@ -182,15 +222,18 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     q, k, v: [B, H, T, D] bf16 or fp32 CUDA tensors (unit stride on D);
     frozen: length-H sequence of 0/1; a, r: fp32 [H, Tp] contiguous.
     """
+    _check_layer_inputs(v, a, r, q=q, k=k, **({} if out is None else {"out": out}))
     B, H, T, D = v.shape
-    if a.dtype != torch.float32 or r.dtype != torch.float32 or not a.is_contiguous() or not r.is_contiguous():
-        raise ValueError("a and r must be contiguous float32 [H, Tp]")
-    if a.shape != r.shape or a.shape[0] != H:
-        raise ValueError("a and r must both be [H, Tp]")
     if out is None:
         out = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    _check_like("lse", lse, v, shape=(B, H, T), dtype=torch.float32)
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, T]")
+    if workspace is not None:
+        _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
+    _require_gpu(v)
     prm = Params(v, frozen, a.shape[1], softmax_scale, events)
     prm.set_strides(q=q, k=k, v=v, o=out)
     ws_n = workspace_bytes(prm, False)
@@ -207,11 +250,15 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
 def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
                         dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
     """Backward of the hybrid layer; returns (dQ, dK, dV)."""
+    given = {n: t for n, t in dict(dq=dq, dk=dk, dv=dv).items() if t is not None}
+    _check_layer_inputs(v, a, r, q=q, k=k, o=o, dout=dout, **given)
     B, H, T, D = v.shape
-    if a.dtype != torch.float32 or r.dtype != torch.float32 or not a.is_contiguous() or not r.is_contiguous():
-        raise ValueError("a and r must be contiguous float32 [H, Tp]")
-    if not lse.is_contiguous() or lse.shape != (B, H, T) or lse.dtype != torch.float32:
+    _check_like("lse", lse, v, shape=(B, H, T), dtype=torch.float32)
+    if not lse.is_contiguous():
         raise ValueError("lse must be contiguous float32 [B, H, T]")
+    if workspace is not None:
+        _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
+    _require_gpu(v)
     mk = lambda: torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)  # noqa: E731
     dq = mk() if dq is None else dq
     dk = mk() if dk is None else dk
@@ -223,15 +270,17 @@ def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=v.device)
     st = LIB.saf_hybrid_attn_bwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                  _ptr(a), _ptr(r), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
-                                 workspace.numel(), _stream_handle(stream))
+                                 workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(st, "saf_hybrid_attn_bwd")
     return dq, dk, dv
 
 
 def saf_pattern_dense(a_h: torch.Tensor, r_h: torch.Tensor, T: int, stream=None) -> torch.Tensor:
     """Dense [T, T] fp32 compact pattern of one frozen head."""
-    if a_h.dtype != torch.float32 or r_h.dtype != torch.float32:
-        raise ValueError("a and r must be float32")
+    if a_h.dtype != torch.float32 or r_h.dtype != torch.float32 or a_h.dim() != 1 or r_h.dim() != 1:
+        raise ValueError("a and r must be float32 vectors [Tp]")
+    if not a_h.is_contiguous() or not r_h.is_contiguous() or a_h.device != r_h.device or not a_h.is_cuda:
+        raise ValueError("a and r must be contiguous vectors on one GPU")
     Tp = min(a_h.numel(), r_h.numel())
     w = torch.empty((T, T), dtype=torch.float32, device=a_h.device)
     _check(LIB.saf_pattern_dense(T, Tp, _ptr(a_h), _ptr(r_h), _ptr(w), _stream_handle(stream)),
@@ -241,8 +290,10 @@ def saf_pattern_dense(a_h: torch.Tensor, r_h: torch.Tensor, T: int, stream=None)
 
 def saf_pattern_lognorm(a: torch.Tensor, r: torch.Tensor, T: int, stream=None) -> torch.Tensor:
     """log N(i) for every row of a, r ([n, Tp] fp32): returns [n, T]."""
-    if a.dtype != torch.float32 or r.dtype != torch.float32 or a.shape != r.shape:
+    if a.dtype != torch.float32 or r.dtype != torch.float32 or a.shape != r.shape or a.dim() != 2:
         raise ValueError("a and r must be float32 [n, Tp]")
+    if a.device != r.device or not a.is_cuda:
+        raise ValueError("a and r must be on one GPU")
     a = a.contiguous()
     r = r.contiguous()
     n, Tp = a.shape

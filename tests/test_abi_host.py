@@ -180,3 +180,35 @@ def test_pattern_entry_points_reject(b):
 def test_binding_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "fixed_pattern_hybrid_amd", "binding.py")).read()
     assert "oracle" not in src and "import numpy" not in src
+
+
+def test_binding_rejects_mismatched_tensors(b):
+    # The library sees only pointers and strides; the binding must refuse
+    # tensors whose shape, dtype or device differs from v's before any call.
+    import torch
+
+    B_, H, T, D = 2, 3, 16, 64
+    mk = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)  # noqa: E731
+    q, k, v = mk(B_, H, T, D), mk(B_, H, T, D), mk(B_, H, T, D)
+    a, r = mk(H, T, dt=torch.float32), mk(H, T, dt=torch.float32)
+    fz = [0, 1, 0]
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_hybrid_attn_fwd(mk(B_, H, T - 1, D), k, v, fz, a, r)
+    with pytest.raises(ValueError, match="dtype"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=mk(B_, H, T, D, dt=torch.float16))
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, lse=mk(B_, H, T + 1, dt=torch.float32))
+    with pytest.raises(ValueError, match="a and r"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a[:2], r[:2])
+    with pytest.raises(ValueError, match="one entry per head"):
+        b.Params(v, [0, 1], T)
+    lse = mk(B_, H, T, dt=torch.float32)
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r, dq=mk(B_, H, T, D // 2))
+    with pytest.raises(ValueError, match="dtype"):
+        b.saf_hybrid_attn_bwd(q, k, v, v, mk(B_, H, T, D, dt=torch.float32), lse, fz, a, r)
+    # well-formed host tensors pass every shape check and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r)
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r)
