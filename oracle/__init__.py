@@ -2,7 +2,8 @@
 
 This package is a plain, slow, dense implementation of what the layer
 computes, written from "When Can Attention Heads Be Statically Defined?"
-(Section 3, Section 3.2 Equation 3, Appendix A.1 Equations 5-7, Appendix D.2).
+(Section 3, Section 3.2 Equation 3, Appendix A.1 Equations 5-7, Appendix D.2,
+and the trainable-pattern gradients of Appendix C.3.2).
 It exists only to check the HIP library.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import it; the library and its Python binding never do, and nothing here
@@ -15,12 +16,14 @@ Every function is pinned by a CPU test to something other than itself
 from .saf_oracle import (
     frozen_head_bwd,
     frozen_head_fwd,
+    frozen_head_pattern_grad,
     frozen_logits,
     frozen_lognorm,
     frozen_pattern,
     frozen_rows_fwd,
     hybrid_bwd,
     hybrid_fwd,
+    hybrid_pattern_grad,
     ordinary_head_bwd,
     ordinary_head_fwd,
     ordinary_rows_fwd,
@@ -30,12 +33,14 @@ from .saf_oracle import (
 __all__ = [
     "frozen_head_bwd",
     "frozen_head_fwd",
+    "frozen_head_pattern_grad",
     "frozen_logits",
     "frozen_lognorm",
     "frozen_pattern",
     "frozen_rows_fwd",
     "hybrid_bwd",
     "hybrid_fwd",
+    "hybrid_pattern_grad",
     "ordinary_head_bwd",
     "ordinary_head_fwd",
     "ordinary_rows_fwd",

@@ -139,6 +139,37 @@ def frozen_head_bwd(do, a, r) -> np.ndarray:
     return dv
 
 
+def frozen_head_pattern_grad(v, do, a, r) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients of a frozen head's pattern parameters, for the variant whose
+    alpha and rho stay trainable (Appendix C.3.2 "Pattern content and
+    trainability"; the pattern of Section 3.2, Equation 3).
+
+    With W = P-hat (row softmax of the logits G_ij = a[j] + r[i-j], j <= i),
+    O = W V and an upstream gradient dO, the chain rule through the row
+    softmax (normaliser included) gives, per row i,
+        dW = dO V^T,   D_i = sum_j W_ij dW_ij,   dG_ij = W_ij (dW_ij - D_i),
+    and since a[j] enters every logit of column j and r[d] every logit of
+    diagonal i - j = d:
+        da[j] = sum_i dG_ij   (column sums),
+        dr[d] = sum_i dG_{i, i-d}   (diagonal sums).
+    Returns (da, dr), each of length T; entries beyond T would be zero.
+    """
+    v = np.asarray(v, dtype=F64)
+    do = np.asarray(do, dtype=F64)
+    T, D = v.shape
+    da = np.zeros(T, dtype=F64)
+    dr = np.zeros(T, dtype=F64)
+    for rows in _rows_chunks(T):
+        W = frozen_pattern(a, r, T, rows)
+        dW = do[rows] @ v.T
+        Drow = (W * dW).sum(axis=1)
+        dG = W * (dW - Drow[:, None])
+        da += dG.sum(axis=0)
+        for n, i in enumerate(rows):
+            dr[: i + 1] += dG[n, i::-1]  # dG[i, i - d] for d = 0..i
+    return da, dr
+
+
 # ---------------------------------------------------------------------------
 # Ordinary heads: Appendix A.1, Equations 5-7.
 # ---------------------------------------------------------------------------
@@ -231,6 +262,29 @@ def hybrid_fwd(q, k, v, frozen, a, r, scale: Optional[float] = None,
         else:
             O[b, h], L[b, h] = ordinary_head_fwd(q[b, h], k[b, h], v[b, h], s)
     return O, L
+
+
+def hybrid_pattern_grad(v, do, frozen, a, r):
+    """Pattern-parameter gradients of every frozen head, summed over the batch.
+
+    v, do: [B, H, T, D]; frozen: [H] flags; a, r: [H, Tp] with Tp >= T.
+    Returns dA, dR of shape [H, T] (float64); rows of ordinary heads are NaN.
+    """
+    B, H, T, D = np.shape(v)
+    if len(frozen) != H or np.shape(a)[0] != H or np.shape(r)[0] != H:
+        raise ValueError("frozen mask, a and r need one entry per head")
+    dA = np.full((H, T), np.nan, dtype=F64)
+    dR = np.full((H, T), np.nan, dtype=F64)
+    for h in range(H):
+        if not frozen[h]:
+            continue
+        dA[h] = 0.0
+        dR[h] = 0.0
+        for b in range(B):
+            ga, gr = frozen_head_pattern_grad(v[b, h], do[b, h], a[h], r[h])
+            dA[h] += ga
+            dR[h] += gr
+    return dA, dR
 
 
 def hybrid_bwd(q, k, v, do, frozen, a, r, scale: Optional[float] = None,

@@ -343,3 +343,113 @@ def test_chunking_does_not_change_result(monkeypatch):
     for x, y in zip(ref, got):
         for xx, yy in zip(x if isinstance(x, tuple) else (x,), y if isinstance(y, tuple) else (y,)):
             np.testing.assert_allclose(yy, xx, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Trainable-pattern gradients (da, dr of frozen heads)
+# --------------------------------------------------------------------------
+
+
+def test_pattern_grad_finite_differences():
+    # L = sum_b <dO_b, O_b(a, r)> differentiated by central differences of the
+    # (separately pinned) forward, entry by entry, batch summed.
+    B, T, D = 2, 9, 5
+    rng = np.random.default_rng(101)
+    v, do = rng.standard_normal((B, 1, T, D)), rng.standard_normal((B, 1, T, D))
+    a, r = rng.standard_normal((1, T)), rng.standard_normal((1, T))
+
+    def loss(aa, rr):
+        O, _ = oracle.hybrid_fwd(v, v, v, [1], aa, rr)
+        return float((O * do).sum())
+
+    dA, dR = oracle.hybrid_pattern_grad(v, do, [1], a, r)
+    h = 1e-6
+    for x, g in ((a, dA), (r, dR)):
+        fd = np.zeros(T)
+        for j in range(T):
+            xp, xm = x.copy(), x.copy()
+            xp[0, j] += h
+            xm[0, j] -= h
+            lp = loss(xp, r) if x is a else loss(a, xp)
+            lm = loss(xm, r) if x is a else loss(a, xm)
+            fd[j] = (lp - lm) / (2 * h)
+        assert np.linalg.norm(fd - g[0]) <= 1e-7 * np.linalg.norm(fd), (fd, g[0])
+
+
+def test_pattern_grad_equals_autograd_of_bias():
+    # A frozen head is softmax attention with logits a[j] + r[i-j]; torch
+    # autograd (float64, CPU) through sdpa with that additive mask gives the
+    # gradient of the mask, whose column and diagonal sums are da and dr.
+    T, D = 40, 6
+    rng = np.random.default_rng(102)
+    a = rng.standard_normal(T)
+    r = -0.05 * np.arange(T) + 0.5 * rng.standard_normal(T)
+    v, do = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    ta = torch.tensor(a, requires_grad=True)
+    tr = torch.tensor(r, requires_grad=True)
+    i = torch.arange(T)[:, None]
+    j = torch.arange(T)[None, :]
+    causal = j <= i
+    bias = torch.where(causal, ta[j.expand(T, T)] + tr[(i - j).clamp(min=0)], torch.tensor(-math.inf, dtype=torch.float64))
+    out = _sdpa(torch.zeros(1, 1, T, D, dtype=torch.float64), torch.zeros(1, 1, T, D, dtype=torch.float64),
+                torch.from_numpy(v)[None, None], 1.0, mask=bias[None, None])
+    out.backward(torch.from_numpy(do)[None, None])
+    da, dr = oracle.frozen_head_pattern_grad(v, do, a, r)
+    np.testing.assert_allclose(da, ta.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dr, tr.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_pattern_grad_closed_form_T2():
+    # T = 2: row 0 has weight 1 (no gradient); row 1 has weights w, 1 - w with
+    # w = sigmoid((a0 + r1) - (a1 + r0)).  With g_j = dO_1 . V_j:
+    # dG_10 = w (1 - w)(g0 - g1) = -dG_11, so da = [c, -c] and dr = [-c, c].
+    a = np.array([0.3, -1.1])
+    r = np.array([0.7, 0.2])
+    v = np.array([[1.0, 2.0], [-0.5, 0.25]])
+    do = np.array([[3.0, -1.0], [0.5, 1.5]])
+    w = 1.0 / (1.0 + math.exp(-((a[0] + r[1]) - (a[1] + r[0]))))
+    g0, g1 = do[1] @ v[0], do[1] @ v[1]
+    c = w * (1 - w) * (g0 - g1)
+    da, dr = oracle.frozen_head_pattern_grad(v, do, a, r)
+    np.testing.assert_allclose(da, [c, -c], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(dr, [-c, c], rtol=1e-14, atol=1e-15)
+
+
+def test_pattern_grad_invariants():
+    # Adding a constant to every a (or every r) leaves each row softmax
+    # unchanged, so both gradients sum to zero; the last key only meets the
+    # last row and the largest offset only the corner entry (i, j) = (T-1, 0).
+    T, D = 64, 8
+    rng = np.random.default_rng(103)
+    v, do = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    a, r = rng.standard_normal(T), rng.standard_normal(T)
+    da, dr = oracle.frozen_head_pattern_grad(v, do, a, r)
+    scale = np.abs(da).sum() + np.abs(dr).sum()
+    assert abs(da.sum()) <= 1e-13 * scale and abs(dr.sum()) <= 1e-13 * scale
+    P = oracle.frozen_pattern(a, r, T)
+    O = P @ v
+    dW = do @ v.T
+    Dl = (do * O).sum(axis=1)  # sum_j W dW = dO . O
+    np.testing.assert_allclose(da[T - 1], P[T - 1, T - 1] * (dW[T - 1, T - 1] - Dl[T - 1]), rtol=1e-12)
+    np.testing.assert_allclose(dr[T - 1], P[T - 1, 0] * (dW[T - 1, 0] - Dl[T - 1]), rtol=1e-12)
+    # ordinary heads get no pattern gradient (NaN rows), batch sums add up
+    vb, dob = rng.standard_normal((3, 2, T, D)), rng.standard_normal((3, 2, T, D))
+    ab, rb = rng.standard_normal((2, T + 5)), rng.standard_normal((2, T + 5))
+    dA, dR = oracle.hybrid_pattern_grad(vb, dob, [0, 1], ab, rb)
+    assert np.all(np.isnan(dA[0])) and np.all(np.isnan(dR[0]))
+    sa = sum(oracle.frozen_head_pattern_grad(vb[b, 1], dob[b, 1], ab[1], rb[1])[0] for b in range(3))
+    np.testing.assert_allclose(dA[1], sa, rtol=1e-13, atol=1e-14)
+
+
+def test_pattern_grad_chunking(monkeypatch):
+    from oracle import saf_oracle
+
+    T, D = 70, 4
+    rng = np.random.default_rng(104)
+    v, do = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    a, r = rng.standard_normal(T), rng.standard_normal(T)
+    ref = saf_oracle.frozen_head_pattern_grad(v, do, a, r)
+    monkeypatch.setattr(saf_oracle, "_CHUNK_ELEMS", 9 * T)
+    got = saf_oracle.frozen_head_pattern_grad(v, do, a, r)
+    for x, y in zip(ref, got):
+        np.testing.assert_allclose(y, x, rtol=1e-13, atol=1e-14)
