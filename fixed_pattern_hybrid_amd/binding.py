@@ -30,6 +30,8 @@ EXPORTED = (
     "saf_hybrid_attn_bwd",
     "saf_hybrid_attn_workspace_bytes",
     "saf_pattern_dense",
+    "saf_pattern_grad",
+    "saf_pattern_grad_workspace_bytes",
     "saf_pattern_lognorm",
     "saf_status_string",
     "saf_version",
@@ -86,6 +88,10 @@ def _load():
     lib.saf_hybrid_attn_bwd.restype = ctypes.c_int
     lib.saf_hybrid_attn_workspace_bytes.argtypes = [pp, ctypes.c_int]
     lib.saf_hybrid_attn_workspace_bytes.restype = sz
+    lib.saf_pattern_grad.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_pattern_grad.restype = ctypes.c_int
+    lib.saf_pattern_grad_workspace_bytes.argtypes = [pp]
+    lib.saf_pattern_grad_workspace_bytes.restype = sz
     lib.saf_pattern_dense.argtypes = [i32, i32, vp, vp, vp, vp]
     lib.saf_pattern_dense.restype = ctypes.c_int
     lib.saf_pattern_lognorm.argtypes = [i32, i32, i32, vp, vp, vp, vp]
@@ -273,6 +279,43 @@ def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
                                  workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(st, "saf_hybrid_attn_bwd")
     return dq, dk, dv
+
+
+def pattern_grad_workspace_bytes(params: Params) -> int:
+    return int(LIB.saf_pattern_grad_workspace_bytes(params.ref()))
+
+
+def saf_pattern_grad(v, o, dout, lse, frozen, a, r, da=None, dr=None, workspace=None,
+                     stream=None, events=None):
+    """Gradients of the frozen heads' a and r (trainable-pattern variant);
+    returns (da, dr), fp32 [H, Tp].  Rows of ordinary heads are left as given
+    (zeros when the outputs are allocated here)."""
+    _check_layer_inputs(v, a, r, o=o, dout=dout)
+    B, H, T, D = v.shape
+    _check_like("lse", lse, v, shape=(B, H, T), dtype=torch.float32)
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, T]")
+    for name, t in (("da", da), ("dr", dr)):
+        if t is not None:
+            _check_like(name, t, a)
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous float32 [H, Tp]")
+    if workspace is not None:
+        _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
+    _require_gpu(v)
+    da = torch.zeros_like(a) if da is None else da
+    dr = torch.zeros_like(r) if dr is None else dr
+    prm = Params(v, frozen, a.shape[1], None, events)
+    prm.set_strides(v=v, o=o, do=dout)
+    ws_n = pattern_grad_workspace_bytes(prm)
+    if workspace is not None:
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
+    st = LIB.saf_pattern_grad(prm.ref(), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(a), _ptr(r),
+                              _ptr(da), _ptr(dr), _ptr(ws), ws_n, _stream_handle(stream))
+    _check(st, "saf_pattern_grad")
+    return da, dr
 
 
 def saf_pattern_dense(a_h: torch.Tensor, r_h: torch.Tensor, T: int, stream=None) -> torch.Tensor:

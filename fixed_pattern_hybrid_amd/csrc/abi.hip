@@ -102,6 +102,25 @@ size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
   return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
 }
 
+// Pattern gradients: D_b of frozen rows; for bf16 also the partial column
+// sums [n_frz][groups][T] and diagonal sums [n_frz][groups][key blocks][T].
+struct PgradWs {
+  size_t delta, da_part, dr_part, total;
+};
+PgradWs pgrad_ws(const saf_attn_params* p, int n_frz) {
+  PgradWs w{0, 0, 0, 0};
+  if (n_frz == 0) return w;
+  w.delta = round_up((size_t)n_frz * p->B * p->T * sizeof(float), 256);
+  if (p->dtype == SAF_BF16) {
+    const size_t groups = (size_t)(p->B + saf::kPgradGroup - 1) / saf::kPgradGroup;
+    const size_t nkb = (size_t)(p->T + saf::kPgradBN - 1) / saf::kPgradBN;
+    w.da_part = round_up((size_t)n_frz * groups * p->T * sizeof(float), 256);
+    w.dr_part = round_up((size_t)n_frz * groups * nkb * p->T * sizeof(float), 256);
+  }
+  w.total = w.delta + w.da_part + w.dr_part;
+  return w;
+}
+
 // Records stage event k when the caller asked for it.
 struct Stages {
   const saf_attn_params* p;
@@ -289,6 +308,70 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
       e = saf::launch_bwd_q_f32(args, p->D, stream);
       if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
     }
+  }
+  return SAF_OK;
+}
+
+size_t saf_pattern_grad_workspace_bytes(const saf_attn_params* p) {
+  int o, f;
+  if (check_params(p, &o, &f) != SAF_OK) return 0;
+  return pgrad_ws(p, f).total;
+}
+
+int saf_pattern_grad(const saf_attn_params* p, const void* v, const void* o, const void* dout,
+                     const float* lse, const float* a, const float* r, float* da, float* dr,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  int n_ord = 0, n_frz = 0;
+  int st = check_params(p, &n_ord, &n_frz);
+  if (st != SAF_OK) return st;
+  if ((st = check_tensor(v, p->v_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
+  if ((st = check_tensor(dout, p->do_stride, p)) != SAF_OK) return st;
+  if (!lse || !a || !r || !da || !dr) return SAF_EINVAL;
+  if (!aligned(lse, 4) || !aligned(a, 4) || !aligned(r, 4) || !aligned(da, 4) || !aligned(dr, 4))
+    return SAF_EINVAL;
+  const PgradWs w = pgrad_ws(p, n_frz);
+  if (w.total > 0 && (!ws || ws_bytes < w.total || !aligned(ws, 256))) return SAF_EWORKSPACE;
+  if (n_frz == 0) return SAF_OK;
+
+  saf::PgradArgs args;
+  std::memset(&args, 0, sizeof(args));
+  args.v = ref(v, p->v_stride);
+  args.o = ref(o, p->o_stride);
+  args.dout = ref(dout, p->do_stride);
+  args.a = a;
+  args.r = r;
+  args.lse = lse;
+  args.da = da;
+  args.dr = dr;
+  char* base = static_cast<char*>(ws);
+  args.delta = reinterpret_cast<float*>(base);
+  args.da_part = w.da_part ? reinterpret_cast<float*>(base + w.delta) : nullptr;
+  args.dr_part = w.dr_part ? reinterpret_cast<float*>(base + w.delta + w.da_part) : nullptr;
+  args.B = p->B;
+  args.H = p->H;
+  args.T = p->T;
+  args.prior_len = p->prior_len;
+  args.n_frz = n_frz;
+  args.frz_group = saf::kPgradGroup;
+  args.n_groups = (p->B + saf::kPgradGroup - 1) / saf::kPgradGroup;
+  args.nkb = (p->T + saf::kPgradBN - 1) / saf::kPgradBN;
+  uint8_t ord[saf::kMaxHeads];
+  fill_heads(p, ord, args.frz_heads, nullptr);
+
+  Stages stg{p, stream};
+  if (stg.mark() != hipSuccess) return SAF_EHIP;
+  const int bf16 = p->dtype == SAF_BF16;
+  hipError_t e = saf::launch_pgrad_delta(args, bf16, p->D, stream);
+  if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+  if (bf16) {
+    e = saf::launch_pgrad_bf16(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+    e = saf::launch_pgrad_reduce(args, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
+  } else {
+    e = saf::launch_pgrad_f32(args, p->D, stream);
+    if (e != hipSuccess || stg.mark() != hipSuccess) return SAF_EHIP;
   }
   return SAF_OK;
 }

@@ -69,6 +69,22 @@ struct BwdArgs {
   uint8_t is_frozen[kMaxHeads];
 };
 
+// Pattern-parameter gradients of frozen heads (both dtypes).
+struct PgradArgs {
+  TensorRef v, o, dout;
+  const float* a;    // [H][prior_len]
+  const float* r;    // [H][prior_len]
+  const float* lse;  // [B][H][T]; frozen rows hold log N
+  float* da;         // [H][prior_len] output
+  float* dr;         // [H][prior_len] output
+  float* delta;      // workspace [n_frz][B][T]: rowsum(dO * O)
+  float* da_part;    // bf16 workspace [n_frz][n_groups][T]
+  float* dr_part;    // bf16 workspace [n_frz][n_groups][nkb][T]
+  int B, H, T, prior_len;
+  int n_frz, frz_group, n_groups, nkb;
+  uint8_t frz_heads[kMaxHeads];
+};
+
 // Normaliser arguments: for each listed head h, logZ over rows [0, T) is
 // written to out[(b * H + h) * T + i] for every b in [0, B).
 struct LognormArgs {
@@ -101,6 +117,16 @@ hipError_t launch_fwd_f32(const FwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_pre_f32(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_kv_f32(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_q_f32(const BwdArgs& args, int D, hipStream_t stream);
+
+// Pattern-parameter gradients: rowsum(dO * O) of frozen rows, then the
+// column/diagonal sums (bf16: key-block programs and a fixed-order reduction;
+// fp32: one thread per output entry).
+hipError_t launch_pgrad_delta(const PgradArgs& args, int dtype_bf16, int D, hipStream_t stream);
+hipError_t launch_pgrad_bf16(const PgradArgs& args, int D, hipStream_t stream);
+hipError_t launch_pgrad_reduce(const PgradArgs& args, hipStream_t stream);
+hipError_t launch_pgrad_f32(const PgradArgs& args, int D, hipStream_t stream);
+constexpr int kPgradGroup = 2;   // batch elements per bf16 program
+constexpr int kPgradBN = 128;    // keys per bf16 program
 
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program

@@ -152,6 +152,38 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k,
 size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd);
 
 /*
+ * Gradients of the frozen heads' pattern parameters, for the variant that
+ * keeps training a and r (Appendix C.3.2 "Pattern content and
+ * trainability"; pattern of Section 3.2, Equation 3).  For every frozen head
+ * h, with W the compact pattern (row softmax of G[i][j] = a[j] + r[i-j] over
+ * j <= i), dW_b = dO_b V_b^T, D_b[i] = sum_d dO_b[i][d] O_b[i][d] and
+ * dG_b[i][j] = W[i][j] (dW_b[i][j] - D_b[i]) (the chain rule through the row
+ * softmax, normaliser included):
+ *   da[h][j] = sum_b sum_{i >= j} dG_b[i][j]       (column sums, 0 <= j < T)
+ *   dr[h][d] = sum_b sum_{i >= d} dG_b[i][i - d]   (diagonal sums, 0 <= d < T)
+ * and entries [T, prior_len) of these rows are set to 0.  Rows of ordinary
+ * heads are not written; with no frozen head nothing is launched.
+ *   v, o, dout : device [B][H][T][D] (o: the forward's output for these
+ *                inputs); strides from p (v_stride, o_stride, do_stride).
+ *                Only frozen heads' slices are read.
+ *   lse        : device fp32 [B][H][T] from the forward (log N on frozen rows).
+ *   a, r       : device fp32 [H][prior_len] (the parameters the forward used).
+ *   da, dr     : device fp32 [H][prior_len] outputs.
+ *   ws         : at least saf_pattern_grad_workspace_bytes(p) bytes, 256-byte
+ *                aligned: per-row D_b, and per key block and batch group
+ *                partial sums, reduced in a fixed order (no atomics; results
+ *                are bitwise deterministic).
+ * After the parameters change, the next forward call recomputes the
+ * normalisers (saf_pattern_lognorm gives them alone).
+ */
+int saf_pattern_grad(const saf_attn_params* p, const void* v, const void* o, const void* dout,
+                     const float* lse, const float* a, const float* r, float* da, float* dr,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes saf_pattern_grad needs (0 for invalid p or no frozen head). */
+size_t saf_pattern_grad_workspace_bytes(const saf_attn_params* p);
+
+/*
  * Dense compact pattern of one frozen head (Section 3.2, Equation 3), as an
  * eager reference: w[i][j] = exp(a[j] + r[i-j] - log N(i)) for j <= i and 0
  * above the diagonal.

@@ -21,6 +21,7 @@ from .saf_oracle import (
     frozen_lognorm,
     frozen_pattern,
     frozen_rows_fwd,
+    frozen_rows_pattern_grad,
     hybrid_bwd,
     hybrid_fwd,
     hybrid_pattern_grad,
@@ -38,6 +39,7 @@ __all__ = [
     "frozen_lognorm",
     "frozen_pattern",
     "frozen_rows_fwd",
+    "frozen_rows_pattern_grad",
     "hybrid_bwd",
     "hybrid_fwd",
     "hybrid_pattern_grad",

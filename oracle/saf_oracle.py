@@ -154,19 +154,34 @@ def frozen_head_pattern_grad(v, do, a, r) -> Tuple[np.ndarray, np.ndarray]:
         dr[d] = sum_i dG_{i, i-d}   (diagonal sums).
     Returns (da, dr), each of length T; entries beyond T would be zero.
     """
-    v = np.asarray(v, dtype=F64)
-    do = np.asarray(do, dtype=F64)
-    T, D = v.shape
+    T = np.shape(v)[0]
     da = np.zeros(T, dtype=F64)
     dr = np.zeros(T, dtype=F64)
     for rows in _rows_chunks(T):
-        W = frozen_pattern(a, r, T, rows)
-        dW = do[rows] @ v.T
-        Drow = (W * dW).sum(axis=1)
-        dG = W * (dW - Drow[:, None])
-        da += dG.sum(axis=0)
-        for n, i in enumerate(rows):
-            dr[: i + 1] += dG[n, i::-1]  # dG[i, i - d] for d = 0..i
+        ga, gr = frozen_rows_pattern_grad(v, do, a, r, rows)
+        da += ga
+        dr += gr
+    return da, dr
+
+
+def frozen_rows_pattern_grad(v, do, a, r, rows: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    """The contribution of query rows ``rows`` to (da, dr) of one frozen head
+    (see frozen_head_pattern_grad).  Key j only meets rows i >= j and offset d
+    only rows i >= d, so for j, d >= min(rows) with rows = [min(rows), T) this
+    is the full gradient entry."""
+    v = np.asarray(v, dtype=F64)
+    do = np.asarray(do, dtype=F64)
+    T = v.shape[0]
+    rows = np.asarray(rows, dtype=np.int64)
+    da = np.zeros(T, dtype=F64)
+    dr = np.zeros(T, dtype=F64)
+    W = frozen_pattern(a, r, T, rows)
+    dW = do[rows] @ v.T
+    Drow = (W * dW).sum(axis=1)
+    dG = W * (dW - Drow[:, None])
+    da += dG.sum(axis=0)
+    for n, i in enumerate(rows):
+        dr[: i + 1] += dG[n, i::-1]  # dG[i, i - d] for d = 0..i
     return da, dr
 
 

@@ -212,3 +212,56 @@ def test_binding_rejects_mismatched_tensors(b):
         b.saf_hybrid_attn_fwd(q, k, v, fz, a, r)
     with pytest.raises(ValueError, match="GPU"):
         b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r)
+
+
+def test_pattern_grad_workspace_and_rejects(b):
+    # bf16: D_b of frozen rows, column partials per batch group and diagonal
+    # partials per (batch group, key block of 128)
+    B_, H, T = 3, 4, 300
+    p, arr = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0])
+    ru = lambda x: -(-x // 256) * 256  # noqa: E731
+    groups, nkb = 2, 3
+    want = ru(2 * B_ * T * 4) + ru(2 * groups * T * 4) + ru(2 * groups * nkb * T * 4)
+    need = b.LIB.saf_pattern_grad_workspace_bytes(ctypes.byref(p))
+    assert need == want
+    p32, a32 = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0], dtype=b.SAF_F32)
+    assert b.LIB.saf_pattern_grad_workspace_bytes(ctypes.byref(p32)) == ru(2 * B_ * T * 4)
+    pord, ao = _params(b, B=B_, H=H, T=T)
+    assert b.LIB.saf_pattern_grad_workspace_bytes(ctypes.byref(pord)) == 0
+    bad, ab = _params(b, D=48)
+    assert b.LIB.saf_pattern_grad_workspace_bytes(ctypes.byref(bad)) == 0
+    args = [FAKE] * 8  # v, o, dout, lse, a, r, da, dr
+    g = b.LIB.saf_pattern_grad
+    assert g(ctypes.byref(p), *args, None, need, None) == -3
+    assert g(ctypes.byref(p), *args, FAKE, need - 1, None) == -3
+    assert g(ctypes.byref(p), *args, FAKE + 16, need, None) == -3
+    for k in range(8):
+        a2 = list(args)
+        a2[k] = None
+        assert g(ctypes.byref(p), *a2, FAKE, need, None) == -1, k
+    a2 = list(args)
+    a2[6] = FAKE + 2  # da misaligned
+    assert g(ctypes.byref(p), *a2, FAKE, need, None) == -1
+    bad2, ab2 = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0], prior_len=T - 1)
+    assert g(ctypes.byref(bad2), *args, FAKE, need, None) == -1
+    # no frozen head: valid, nothing to do, no workspace needed
+    assert g(ctypes.byref(pord), *args, None, 0, None) == 0
+
+
+def test_binding_pattern_grad_checks(b):
+    import torch
+
+    B_, H, T, D = 2, 3, 16, 64
+    mk = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)  # noqa: E731
+    v, o, do = mk(B_, H, T, D), mk(B_, H, T, D), mk(B_, H, T, D)
+    a, r = mk(H, T, dt=torch.float32), mk(H, T, dt=torch.float32)
+    lse = mk(B_, H, T, dt=torch.float32)
+    fz = [0, 1, 0]
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_pattern_grad(v, mk(B_, H, T - 1, D), do, lse, fz, a, r)
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_pattern_grad(v, o, do, lse, fz, a, r, da=mk(H, T + 1, dt=torch.float32))
+    with pytest.raises(ValueError, match="dtype"):
+        b.saf_pattern_grad(v, o, do, lse, fz, a, r, dr=mk(H, T, dt=torch.float64))
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_pattern_grad(v, o, do, lse, fz, a, r)

@@ -453,3 +453,16 @@ def test_pattern_grad_chunking(monkeypatch):
     got = saf_oracle.frozen_head_pattern_grad(v, do, a, r)
     for x, y in zip(ref, got):
         np.testing.assert_allclose(y, x, rtol=1e-13, atol=1e-14)
+
+
+def test_pattern_grad_tail_rows_give_tail_entries():
+    # Key j and offset d are only met by rows i >= j (resp. i >= d): the rows
+    # [T0, T) alone give the full entries j, d >= T0.
+    T, D, T0 = 90, 4, 71
+    rng = np.random.default_rng(105)
+    v, do = rng.standard_normal((T, D)), rng.standard_normal((T, D))
+    a, r = rng.standard_normal(T), rng.standard_normal(T)
+    da, dr = oracle.frozen_head_pattern_grad(v, do, a, r)
+    ta, tr_ = oracle.frozen_rows_pattern_grad(v, do, a, r, np.arange(T0, T))
+    np.testing.assert_allclose(ta[T0:], da[T0:], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(tr_[T0:], dr[T0:], rtol=1e-12, atol=1e-14)
