@@ -155,6 +155,53 @@ def per_head_costs(B, cfg, reps: int = 10):
     return out
 
 
+def trainable_pattern_leg(B, cfg, t, stream, reps: int = 20):
+    """Cost of the frozen heads' pattern gradients (the variant whose a and r
+    keep training): saf_pattern_grad after the timed steps, with its kernels
+    bracketed by the library's stage events.  Not part of the headline step."""
+    import numpy as np
+    import torch
+
+    names = ["pg_delta", "pg_kv", "pg_reduce"] if cfg.dtype == "bf16" else ["pg_delta", "pg_f32"]
+    da, dr = torch.zeros_like(t["a"]), torch.zeros_like(t["r"])
+    prm = B.Params(t["v"], t["fz"], t["a"].shape[1])
+    prm.set_strides(v=t["v"], o=t["o"], do=t["do"])
+    ws = torch.empty(max(B.pattern_grad_workspace_bytes(prm), 256), dtype=torch.uint8, device="cuda")
+
+    def call(evs=None):
+        B.saf_pattern_grad(t["v"], t["o"], t["do"], t["lse"], t["fz"], t["a"], t["r"], da=da, dr=dr,
+                           workspace=ws, stream=stream, events=evs)
+
+    for _ in range(3):
+        call()
+    evs = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        for x in e:
+            x.record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s_ in range(reps):
+        call(evs[s_])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    kms = {n: float(np.mean([evs[s_][x].elapsed_time(evs[s_][x + 1]) for s_ in range(reps)]))
+           for x, n in enumerate(names)}
+    n_frz = len(cfg.frozen)
+    fl = pairs(cfg.T) * cfg.D * 2 * cfg.B * n_frz  # dW = dO V^T over the causal pairs
+    kern = "pg_kv" if cfg.dtype == "bf16" else "pg_f32"
+    ach = fl / (kms[kern] * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "kernel_ms": {n: round(x, 4) for n, x in kms.items()},
+            "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "kernel": kern,
+                         "flops_per_launch": fl},
+            "note": "gradients of a and r for the frozen heads (trainable-pattern variant), one call per "
+                    "step after the layer's backward; not included in value"}
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     """Time the float64 oracle on whole heads of the workload (host cores)."""
     import numpy as np
@@ -221,6 +268,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-per-head", action="store_true")
+    ap.add_argument("--no-pattern-grad", action="store_true",
+                    help="skip the trainable-pattern leg (gradients of a and r, reported apart from value)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -343,6 +392,10 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
+    if not args.no_pattern_grad and do is not None and has_frz:
+        tp = trainable_pattern_leg(B, cfg, dict(v=v, o=o, do=do, lse=lse, a=a, r=r, fz=fz), stream)
+        tp["over_layer_step"] = round(tp["ms"] / ms, 4)
+        out["trainable_pattern"] = tp
     if not args.no_per_head and do is not None:
         out["per_head"] = per_head_costs(B, cfg)
     if not args.no_cpu_baseline:

@@ -102,8 +102,16 @@ size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
   return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
 }
 
-// Pattern gradients: D_b of frozen rows; for bf16 also the partial column
-// sums [n_frz][groups][T] and diagonal sums [n_frz][groups][key blocks][T].
+// Pattern gradients: D_b of frozen rows; for bf16 also, per program (frozen
+// head, batch group, key block, query chunk), the partial column sums and
+// diagonal sums.
+size_t pgrad_programs(const saf_attn_params* p, int n_frz) {
+  const size_t groups = (size_t)(p->B + saf::kPgradGroup - 1) / saf::kPgradGroup;
+  const size_t nkb = (size_t)(p->T + saf::kPgradBN - 1) / saf::kPgradBN;
+  const size_t nch = (size_t)(p->T + saf::kPgradQC - 1) / saf::kPgradQC;
+  return (size_t)n_frz * groups * nkb * nch;
+}
+
 struct PgradWs {
   size_t delta, da_part, dr_part, total;
 };
@@ -112,10 +120,9 @@ PgradWs pgrad_ws(const saf_attn_params* p, int n_frz) {
   if (n_frz == 0) return w;
   w.delta = round_up((size_t)n_frz * p->B * p->T * sizeof(float), 256);
   if (p->dtype == SAF_BF16) {
-    const size_t groups = (size_t)(p->B + saf::kPgradGroup - 1) / saf::kPgradGroup;
-    const size_t nkb = (size_t)(p->T + saf::kPgradBN - 1) / saf::kPgradBN;
-    w.da_part = round_up((size_t)n_frz * groups * p->T * sizeof(float), 256);
-    w.dr_part = round_up((size_t)n_frz * groups * nkb * p->T * sizeof(float), 256);
+    const size_t progs = pgrad_programs(p, n_frz);
+    w.da_part = round_up(progs * saf::kPgradBN * sizeof(float), 256);
+    w.dr_part = round_up(progs * saf::kPgradDiag * sizeof(float), 256);
   }
   w.total = w.delta + w.da_part + w.dr_part;
   return w;
@@ -330,6 +337,8 @@ int saf_pattern_grad(const saf_attn_params* p, const void* v, const void* o, con
   if (!lse || !a || !r || !da || !dr) return SAF_EINVAL;
   if (!aligned(lse, 4) || !aligned(a, 4) || !aligned(r, 4) || !aligned(da, 4) || !aligned(dr, 4))
     return SAF_EINVAL;
+  // bf16: one program per (frozen head, batch group, key block, query chunk)
+  if (p->dtype == SAF_BF16 && pgrad_programs(p, n_frz) > (size_t)INT32_MAX) return SAF_EUNSUPPORTED;
   const PgradWs w = pgrad_ws(p, n_frz);
   if (w.total > 0 && (!ws || ws_bytes < w.total || !aligned(ws, 256))) return SAF_EWORKSPACE;
   if (n_frz == 0) return SAF_OK;
@@ -356,6 +365,7 @@ int saf_pattern_grad(const saf_attn_params* p, const void* v, const void* o, con
   args.frz_group = saf::kPgradGroup;
   args.n_groups = (p->B + saf::kPgradGroup - 1) / saf::kPgradGroup;
   args.nkb = (p->T + saf::kPgradBN - 1) / saf::kPgradBN;
+  args.nch = (p->T + saf::kPgradQC - 1) / saf::kPgradQC;
   uint8_t ord[saf::kMaxHeads];
   fill_heads(p, ord, args.frz_heads, nullptr);
 

@@ -10,19 +10,23 @@
 //
 // Kernels (in launch order):
 //   pg_delta  : D_b[i] for frozen rows, one thread per row.
-//   pg_kv     (bf16) one program per (key block of 128, frozen head, batch
-//             group of two), four waves of 32 keys; query tiles of 64 stream
-//             through LDS as in the key-block pass of the backward.  Each lane
-//             owns a key: the accumulator of dW^T-like products C[query][key]
-//             is seeded with -(D_b0 + D_b1) and collects dO_b V_b^T of both
-//             batch elements, so that W (shared by the group) multiplies it
-//             once.  Column sums stay in the lane; diagonal sums go through
-//             LDS rings (one per half-wave, 256 offsets; the 32 lanes of a
-//             half-wave hit distinct offsets in every instruction, so the
-//             adds need no ordering between lanes) and are flushed, summed in
-//             a fixed order, once no later tile can reach them.
-//   pg_reduce (bf16) sums the partials of the key blocks and batch groups in
-//             a fixed order and writes da, dr (zeros from T to prior_len).
+//   pg_kv     (bf16) one program per (frozen head, batch group of two, key
+//             block of 128, chunk of 512 queries), four waves of 32 keys;
+//             query tiles of 64 stream through LDS as in the key-block pass of
+//             the backward.  Each lane owns a key: the accumulator of
+//             C[query][key] products is seeded with -(D_b0 + D_b1) and
+//             collects dO_b V_b^T of both batch elements, so that W (shared by
+//             the group) multiplies it once.  Column sums stay in the lane.
+//             Diagonal sums: within a 32 x 32 block a cross-lane permute
+//             rotates register r of lane t to lane t - m_r, m_r being the
+//             block row of register r, after which lane t holds terms of two
+//             diagonals only (i - j = -t or 32 - t relative to the block);
+//             those sums go into a per-wave LDS array over the chunk's
+//             offsets (plain adds, no atomics), summed over the waves in a
+//             fixed order at the end.
+//   pg_reduce (bf16) sums the partials of the chunks, key blocks and batch
+//             groups in a fixed order and writes da, dr (zeros from T to
+//             prior_len).
 //   pg_f32    (fp32) one thread per output entry, looping over rows.
 #include "saf_internal.h"
 #include "saf_tile.h"
@@ -33,7 +37,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kBM = 64;         // queries per tile
 constexpr int kBN = kPgradBN;   // keys per program
-constexpr int kRing = 256;      // offsets per diagonal ring (power of two)
+constexpr int kQC = kPgradQC;   // queries per program (a chunk of the key block's rows)
+constexpr int kDiag = kPgradDiag;  // offsets i - j a program can meet: kQC + kBN - 1, padded
 
 template <int D>
 struct PgCfg {
@@ -45,7 +50,7 @@ struct PgCfg {
   static constexpr int BSTRIDE = band_stride(BAND);
   // per buffer: z2[BM], -sum_b D_b [BM], then 4 shifted copies of the r band
   static constexpr int FSTRIDE = 2 * kBM + 4 * BSTRIDE;
-  static constexpr size_t lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4 + size_t(8) * kRing * 4;
+  static constexpr size_t lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4 + size_t(4) * kDiag * 4;
 };
 
 // D_b[i] = sum_d dO[b][h][i][d] * O[b][h][i][d] of frozen heads; E is the
@@ -83,24 +88,25 @@ __global__ __launch_bounds__(kThreads) void pg_delta_kernel(PgradArgs A) {
   A.delta[(int64_t)hb * A.T + i] = s;
 }
 
-// Key-block program (frozen head hidx, batch group grp, key block kb).
+// Program (frozen head hidx, batch group grp, key block kb, query chunk ch).
 // NG: batch elements it covers (the group size, or 1 for a final group of
 // one).
 template <int D, int NG>
-__device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp, int kb, lds_bf16* smem) {
+__device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp, int kb, int ch, lds_bf16* smem) {
   using C = PgCfg<D>;
   constexpr int G = NG;     // batch elements computed
   constexpr int GL = C::G;  // batch slots of the LDS layout
-  const int l = lane_id(), w = wave_id(), hl = l >> 5;
+  const int l = lane_id(), w = wave_id(), hl = l >> 5, t = l & 31;
   const int T = A.T;
   const int k0 = kb * kBN;
-  const int j = k0 + 32 * w + (l & 31);  // this lane's key
+  const int j = k0 + 32 * w + t;  // this lane's key
   const int wk_lo = k0 + 32 * w;
   const int b0 = grp * GL;
   const int h = A.frz_heads[hidx];
   const float* arow = A.a + (int64_t)h * A.prior_len;
   const float* rrow = A.r + (int64_t)h * A.prior_len;
   const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
+  const int64_t prog = (((int64_t)hidx * A.n_groups + grp) * A.nkb + kb) * A.nch + ch;
 
   // V rows of this lane's key, one per batch element, as B operands
   // (col = key, k = d).
@@ -114,15 +120,31 @@ __device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp
                            : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   }
 
-  // LDS: dO tiles [buf][gb]; per buffer z2, -sum D and the band; then the
-  // eight diagonal rings (wave w, half-wave hl at ring 2w + hl).
-  lds_f32* fb = (lds_f32*)(smem + 2 * GL * C::TILE);
-  lds_f32* ring = fb + 2 * C::FSTRIDE;
-  for (int x = threadIdx.x; x < 8 * kRing; x += kThreads) ring[x] = 0.f;
-  lds_f32* myring = ring + (2 * w + hl) * kRing;
+  // Register r of a 32 x 32 C block holds block row m_r = 8(r/4) + 4hl + r%4.
+  // Lane t takes register r from lane (t + m_r) mod 32 of its half-wave: the
+  // term of key t + m_r (row m_r), on diagonal m_r - (t + m_r) = -t, or 32 - t
+  // when t + m_r wraps past 31.
+  int src[16];
+  bool nowrap[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = 8 * (r >> 2) + 4 * hl + (r & 3);
+    src[r] = (((t + m) & 31) + 32 * hl) * 4;
+    nowrap[r] = t + m < 32;
+  }
 
-  const int qt0 = k0 / kBM;  // < nqt since k0 < T
-  const int nqt = (T + kBM - 1) / kBM;
+  // LDS: dO tiles [buf][gb]; per buffer z2, -sum D and the band; then one
+  // array per wave over the chunk's offsets: entry x is offset
+  // ch * QC - (BN - 1) + x.
+  lds_f32* fb = (lds_f32*)(smem + 2 * GL * C::TILE);
+  lds_f32* diag = fb + 2 * C::FSTRIDE;
+  for (int x = threadIdx.x; x < 4 * kDiag; x += kThreads) diag[x] = 0.f;
+  lds_f32* mydiag = diag + w * kDiag;
+
+  const int q_start = k0 + ch * kQC;  // < T (the grid skips empty chunks)
+  const int q_end = min(q_start + kQC, T);
+  const int qt0 = q_start / kBM;
+  const int nqt = (q_end + kBM - 1) / kBM;
   const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, the same for every b
   const float* dl = A.delta + ((int64_t)hidx * A.B + b0) * T;
 
@@ -154,22 +176,6 @@ __device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp
     band.store(zs + 2 * kBM);
     wait_vm_loads();
   };
-  // Offsets [lo, hi] are complete: sum the eight rings in a fixed order,
-  // write the partial and clear the slots for the offsets 256 further on.
-  float* drp = A.dr_part + (((int64_t)hidx * A.n_groups + grp) * A.nkb + kb) * T;
-  auto flush = [&](int lo, int hi) {
-    const int x = (lo > 0 ? lo : 0) + (int)threadIdx.x;
-    if (x <= hi) {
-      const int slot = x & (kRing - 1);
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        s += ring[q * kRing + slot];
-        ring[q * kRing + slot] = 0.f;
-      }
-      if (x < T) drp[x] = s;
-    }
-  };
 
   load_next(qt0 * kBM, 0);
   store_next(0);
@@ -190,7 +196,7 @@ __device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp
       const int xj = (kBN - 1) - (j - k0);
       const int cpy = xj & 3;
       const lds_f32* rc = rs + cpy * C::BSTRIDE - cpy;
-      const int dbase = i0 - j;  // offset i - j of tile row 0
+      float tot[2], nw[2];  // per block: all rotated terms, the unwrapped ones
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         // acc[query][key] = sum_b (dO_b V_b^T - D_b): C register r holds row
@@ -207,6 +213,8 @@ __device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp
 #pragma unroll
           for (int ks = 0; ks < C::NKS; ++ks)
             acc = mfma32(lds_frag_nat<D>(smem + (bi * GL + gb) * C::TILE, 32 * c, 16 * ks), vf[gb][ks], acc);
+        tot[c] = 0.f;
+        nw[c] = 0.f;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int base = 32 * c + 8 * q4 + 4 * hl;  // first of four tile rows
@@ -214,60 +222,107 @@ __device__ __forceinline__ void pg_program(const PgradArgs& A, int hidx, int grp
           const f32x4 r4 = lds_read_f4(rc + base + xj);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float g = fast_exp2(a2 + r4[e] - z4[e]) * acc[4 * q4 + e];  // sum_b dG_b[i][j]
+            const int r = 4 * q4 + e;
+            const float g = fast_exp2(a2 + r4[e] - z4[e]) * acc[r];  // sum_b dG_b[i][j]
             colsum += g;
-            __hip_atomic_fetch_add(myring + ((dbase + base + e) & (kRing - 1)), g, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            const float x = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src[r], __builtin_bit_cast(int, g)));
+            tot[c] += x;
+            nw[c] += nowrap[r] ? x : 0.f;
           }
         }
+      }
+      // Offsets relative to (i0 - jw): -t (block 0 unwrapped), 32 - t (block
+      // 0 wrapped, block 1 unwrapped), 64 - t (block 1 wrapped); the two
+      // half-waves hold the same offsets for their rows.
+      float s0 = nw[0], s1 = (tot[0] - nw[0]) + nw[1], s2 = tot[1] - nw[1];
+      s0 += xor32(s0);
+      s1 += xor32(s1);
+      s2 += xor32(s2);
+      if (hl == 0) {
+        const int x0 = (i0 - q_start) - 32 * w + (kBN - 1) - t;  // entry of offset i0 - jw - t
+        mydiag[x0] += s0;
+        mydiag[x0 + 32] += s1;
+        mydiag[x0 + 64] += s2;
       }
     }
     if (more) store_next(bi ^ 1);
     __syncthreads();
-    // Later tiles reach offsets >= i0 + BM - k0 - (BN - 1) only; the last
-    // tile completes every offset it touched.  The cleared slots are next
-    // used two tiles on, after another barrier.
-    flush(i0 - k0 - (kBN - 1), more ? i0 + kBM - k0 - kBN : i0 + kBM - 1 - k0);
   }
-  // this lane's key column: the two half-waves hold different rows
-  const float tot = colsum + xor32(colsum);
-  if (hl == 0 && j < T) A.da_part[((int64_t)hidx * A.n_groups + grp) * T + j] = tot;
+  // diagonal partials: the four waves summed in a fixed order
+  float* drp = A.dr_part + prog * kDiag;
+  for (int x = threadIdx.x; x < kDiag; x += kThreads)
+    drp[x] = ((diag[x] + diag[kDiag + x]) + diag[2 * kDiag + x]) + diag[3 * kDiag + x];
+  // this lane's key column over the chunk: the two half-waves hold different rows
+  const float ctot = colsum + xor32(colsum);
+  if (hl == 0) A.da_part[prog * kBN + (j - k0)] = ctot;
 }
 
-// One launch: program p -> (key block, slot), key block 0 (most queries)
-// first.
+// One launch: program p -> (chunk, key block, frozen head, batch group), the
+// chunk index slowest; chunks past a key block's last row exit at once.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void pg_kv_kernel(PgradArgs A) {
   SAF_DYN_LDS(smem);
-  const int per_k = A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / per_k;
-  const int f = blockIdx.x - kb * per_k;
+  const int per_c = A.nkb * A.n_frz * A.n_groups;
+  const int ch = blockIdx.x / per_c;
+  int f = blockIdx.x - ch * per_c;
+  const int kb = f / (A.n_frz * A.n_groups);
+  f -= kb * (A.n_frz * A.n_groups);
   const int hidx = f / A.n_groups, grp = f - hidx * A.n_groups;
-  if (A.B - grp * PgCfg<D>::G >= PgCfg<D>::G) pg_program<D, PgCfg<D>::G>(A, hidx, grp, kb, smem);
-  else pg_program<D, 1>(A, hidx, grp, kb, smem);
+  if (kb * kBN + ch * kQC >= A.T) return;
+  if (A.B - grp * PgCfg<D>::G >= PgCfg<D>::G) pg_program<D, PgCfg<D>::G>(A, hidx, grp, kb, ch, smem);
+  else pg_program<D, 1>(A, hidx, grp, kb, ch, smem);
 }
 
-// da[h][x], dr[h][x] for x < prior_len: fixed-order sums of the partials
-// (key blocks whose keys reach offset x, i.e. kb <= (T - 1 - x) / BN).
+// da[h][x], dr[h][x] for x < prior_len: fixed-order sums of the partials of
+// the programs that met key x (key block x / BN, every chunk) or offset x
+// (chunks whose window [ch QC - (BN - 1), ch QC + QC - 1] holds x, in key
+// blocks that reach it: kb <= (T - 1 - x) / BN).  A block covers 32 entries
+// of one head with eight threads per entry: thread part p takes the chunks
+// ch = p mod 8 (da) and the key blocks kb = p mod 8 (dr, four independent
+// running sums so that loads overlap), and the parts are added in order.
+constexpr int kRedX = 32;
+constexpr int kRedP = kThreads / kRedX;
 __global__ __launch_bounds__(kThreads) void pg_reduce_kernel(PgradArgs A) {
-  const int nxb = (A.prior_len + kThreads - 1) / kThreads;
+  __shared__ float part[2][kRedP][kRedX];
+  const int nxb = (A.prior_len + kRedX - 1) / kRedX;
   const int hidx = blockIdx.x / nxb;
-  const int x = (blockIdx.x - hidx * nxb) * kThreads + threadIdx.x;
-  if (x >= A.prior_len) return;
-  const int h = A.frz_heads[hidx];
+  const int xi = threadIdx.x % kRedX, wp = threadIdx.x / kRedX;
+  const int x = (blockIdx.x - hidx * nxb) * kRedX + xi;
   const int T = A.T;
   float da = 0.f, dr = 0.f;
   if (x < T) {
+    const int kbx = x / kBN;
+    const int nch_x = (T - kbx * kBN + kQC - 1) / kQC;
     const int kbmax = (T - 1 - x) / kBN;
-    for (int grp = 0; grp < A.n_groups; ++grp) {
-      const int64_t g = (int64_t)hidx * A.n_groups + grp;
-      da += A.da_part[g * T + x];
-      const float* p = A.dr_part + g * A.nkb * T + x;
-      for (int kb = 0; kb <= kbmax; ++kb) dr += p[(int64_t)kb * T];
+    const int ch_lo = x + (kBN - 1) - (kDiag - 1) > 0 ? (x + (kBN - 1) - (kDiag - 1) + kQC - 1) / kQC : 0;
+    const int ch_hi = (x + (kBN - 1)) / kQC;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < A.n_groups; ++g) {
+      const int64_t gk = ((int64_t)hidx * A.n_groups + g) * A.nkb;
+      for (int ch = wp; ch < nch_x; ch += kRedP) da += A.da_part[((gk + kbx) * A.nch + ch) * kBN + (x - kbx * kBN)];
+      int u = 0;
+      for (int kb = wp; kb <= kbmax; kb += kRedP, u = (u + 1) & 3) {
+        for (int ch = ch_lo; ch <= ch_hi; ++ch)
+          if (ch * kQC + kb * kBN < T)  // the chunk exists in this key block
+            acc[u] += A.dr_part[((gk + kb) * A.nch + ch) * kDiag + (x - ch * kQC + (kBN - 1))];
+      }
     }
+    dr = (acc[0] + acc[1]) + (acc[2] + acc[3]);
   }
-  A.da[(int64_t)h * A.prior_len + x] = da;
-  A.dr[(int64_t)h * A.prior_len + x] = dr;
+  part[0][wp][xi] = da;
+  part[1][wp][xi] = dr;
+  __syncthreads();
+  if (wp == 0 && x < A.prior_len) {
+    const int h = A.frz_heads[hidx];
+    float sa = 0.f, sr = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRedP; ++q) {
+      sa += part[0][q][xi];
+      sr += part[1][q][xi];
+    }
+    A.da[(int64_t)h * A.prior_len + x] = sa;
+    A.dr[(int64_t)h * A.prior_len + x] = sr;
+  }
 }
 
 // fp32: one thread per output entry x of one frozen head; blocks
@@ -312,7 +367,7 @@ hipError_t launch_pgrad_bf16_d(PgradArgs args, hipStream_t stream) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(pg_kv_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds);
   if (attr != hipSuccess) return attr;
-  const int64_t grid = (int64_t)args.nkb * args.n_frz * args.n_groups;
+  const int64_t grid = (int64_t)args.nch * args.nkb * args.n_frz * args.n_groups;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(pg_kv_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::lds, stream, args);
   return hipGetLastError();
@@ -365,7 +420,7 @@ hipError_t launch_pgrad_bf16(const PgradArgs& args, int D, hipStream_t stream) {
 }
 
 hipError_t launch_pgrad_reduce(const PgradArgs& args, hipStream_t stream) {
-  const int64_t grid = (int64_t)args.n_frz * ((args.prior_len + kThreads - 1) / kThreads);
+  const int64_t grid = (int64_t)args.n_frz * ((args.prior_len + kRedX - 1) / kRedX);
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(pg_reduce_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, args);
   return hipGetLastError();

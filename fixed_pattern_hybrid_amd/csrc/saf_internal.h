@@ -78,10 +78,12 @@ struct PgradArgs {
   float* da;         // [H][prior_len] output
   float* dr;         // [H][prior_len] output
   float* delta;      // workspace [n_frz][B][T]: rowsum(dO * O)
-  float* da_part;    // bf16 workspace [n_frz][n_groups][T]
-  float* dr_part;    // bf16 workspace [n_frz][n_groups][nkb][T]
+  // bf16 workspace, one row per program (frozen head, batch group, key
+  // block, query chunk): column sums [kPgradBN] and diagonal sums [kPgradDiag]
+  float* da_part;
+  float* dr_part;
   int B, H, T, prior_len;
-  int n_frz, frz_group, n_groups, nkb;
+  int n_frz, frz_group, n_groups, nkb, nch;
   uint8_t frz_heads[kMaxHeads];
 };
 
@@ -127,6 +129,8 @@ hipError_t launch_pgrad_reduce(const PgradArgs& args, hipStream_t stream);
 hipError_t launch_pgrad_f32(const PgradArgs& args, int D, hipStream_t stream);
 constexpr int kPgradGroup = 2;   // batch elements per bf16 program
 constexpr int kPgradBN = 128;    // keys per bf16 program
+constexpr int kPgradQC = 512;    // queries per bf16 program
+constexpr int kPgradDiag = 640;  // offsets per program: kPgradQC + kPgradBN - 1, padded
 
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program

@@ -215,13 +215,14 @@ def test_binding_rejects_mismatched_tensors(b):
 
 
 def test_pattern_grad_workspace_and_rejects(b):
-    # bf16: D_b of frozen rows, column partials per batch group and diagonal
-    # partials per (batch group, key block of 128)
-    B_, H, T = 3, 4, 300
+    # bf16: D_b of frozen rows, then per program (frozen head, batch group of
+    # 2, key block of 128, query chunk of 512) 128 column and 640 diagonal
+    # partial sums
+    B_, H, T = 3, 4, 600
     p, arr = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0])
     ru = lambda x: -(-x // 256) * 256  # noqa: E731
-    groups, nkb = 2, 3
-    want = ru(2 * B_ * T * 4) + ru(2 * groups * T * 4) + ru(2 * groups * nkb * T * 4)
+    progs = 2 * 2 * 5 * 2
+    want = ru(2 * B_ * T * 4) + ru(progs * 128 * 4) + ru(progs * 640 * 4)
     need = b.LIB.saf_pattern_grad_workspace_bytes(ctypes.byref(p))
     assert need == want
     p32, a32 = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0], dtype=b.SAF_F32)
@@ -244,6 +245,9 @@ def test_pattern_grad_workspace_and_rejects(b):
     assert g(ctypes.byref(p), *a2, FAKE, need, None) == -1
     bad2, ab2 = _params(b, B=B_, H=H, T=T, frozen=[0, 1, 1, 0], prior_len=T - 1)
     assert g(ctypes.byref(bad2), *args, FAKE, need, None) == -1
+    # more than 2^31 - 1 programs (B*H*T within the layer's limits)
+    big, abig = _params(b, B=256, H=256, T=1 << 20, frozen=[1] * 256)
+    assert g(ctypes.byref(big), *args, FAKE, 1 << 62, None) == -2
     # no frozen head: valid, nothing to do, no workspace needed
     assert g(ctypes.byref(pord), *args, None, 0, None) == 0
 
