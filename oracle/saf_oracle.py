@@ -248,7 +248,7 @@ def ordinary_head_bwd(q, k, v, do, scale: float) -> Tuple[np.ndarray, np.ndarray
 
 
 def _check(q, v, frozen, a, r):
-    B, H, T, D = np.shape(v)
+    B, H, T, D = np.shape(q)
     if len(frozen) != H:
         raise ValueError("frozen mask length must equal H")
     if np.shape(a)[0] != H or np.shape(r)[0] != H:
@@ -256,26 +256,39 @@ def _check(q, v, frozen, a, r):
     return B, H, T, D
 
 
+def _kv_group(q, k, v) -> int:
+    """Query heads per key/value head.  Grouped-query attention (the pages'
+    Qwen path, Appendix D.2): query head h uses key/value head h // group."""
+    H, Hk = np.shape(q)[1], np.shape(k)[1]
+    if np.shape(v)[1] != Hk or Hk < 1 or H % Hk != 0:
+        raise ValueError("k and v need the same number of heads, dividing the query heads")
+    return H // Hk
+
+
 def hybrid_fwd(q, k, v, frozen, a, r, scale: Optional[float] = None,
                heads: Optional[Iterable[Tuple[int, int]]] = None):
     """Forward of the hybrid layer.
 
-    q, k, v: [B, H, T, D]; frozen: [H] flags; a, r: [H, Tp] with Tp >= T.
+    q: [B, H, T, D]; k, v: [B, Hkv, T, D] with Hkv dividing H (Hkv = H for
+    multi-head attention; otherwise query head h uses key/value head
+    h // (H / Hkv), the grouped-query path of the pages' Qwen experiments);
+    frozen: [H] flags; a, r: [H, Tp] with Tp >= T.
     Returns O [B, H, T, D] and L [B, H, T] in float64.  For frozen heads L is
     log N(i), the same for every batch element, and q, k are never read.
     ``heads`` restricts the work to the listed (b, h) pairs; other entries of
     the outputs are NaN.
     """
     B, H, T, D = _check(q, v, frozen, a, r)
+    g = _kv_group(q, k, v)
     s = default_scale(D) if scale is None else float(scale)
     O = np.full((B, H, T, D), np.nan, dtype=F64)
     L = np.full((B, H, T), np.nan, dtype=F64)
     todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in todo:
         if frozen[h]:
-            O[b, h], L[b, h] = frozen_head_fwd(v[b, h], a[h], r[h])
+            O[b, h], L[b, h] = frozen_head_fwd(v[b, h // g], a[h], r[h])
         else:
-            O[b, h], L[b, h] = ordinary_head_fwd(q[b, h], k[b, h], v[b, h], s)
+            O[b, h], L[b, h] = ordinary_head_fwd(q[b, h], k[b, h // g], v[b, h // g], s)
     return O, L
 
 
@@ -306,9 +319,12 @@ def hybrid_bwd(q, k, v, do, frozen, a, r, scale: Optional[float] = None,
                heads: Optional[Iterable[Tuple[int, int]]] = None):
     """Backward of the hybrid layer given dO: returns dQ, dK, dV (float64).
 
-    Frozen heads get dQ = dK = 0 exactly and dV = P-hat^T dO.
+    Frozen heads get dQ = dK = 0 exactly and dV = P-hat^T dO.  Multi-head
+    attention only (k, v with H heads).
     """
     B, H, T, D = _check(q, v, frozen, a, r)
+    if _kv_group(q, k, v) != 1:
+        raise ValueError("the backward is defined here for multi-head attention only")
     s = default_scale(D) if scale is None else float(scale)
     dq = np.full((B, H, T, D), np.nan, dtype=F64)
     dk = np.full((B, H, T, D), np.nan, dtype=F64)

@@ -8,7 +8,10 @@ and the distributions of the synthetic inputs.  The shapes follow the pages:
 * the 1B model's per-GPU share at 8K context (16 heads, B=2 per rank),
   Appendix C.5 / Table 23 -- head dimension 128 is used here;
 * the mixed-head numerical check of Appendix D.2 (B=2, T=129, H=4, d=64,
-  stored prior length 192, heads 1 and 3 frozen, zero-based).
+  stored prior length 192, heads 1 and 3 frozen, zero-based);
+* the Qwen3-4B grouped-query prefill of Appendix C.6.2 / Table 26 (32 query
+  heads sharing 8 key/value heads, d=128, B in {4, 8}, T in {2048, 4096,
+  8192}, forward only).
 
 Token content does not change attention cost, so Gaussian inputs of these
 shapes stand in for the pages' FineWeb-Edu activations.
@@ -37,6 +40,11 @@ class Config:
     prior_len: Optional[int] = None  # stored length Tp of a and r (>= T); None -> T
     bwd: bool = True  # whether the workload includes the backward pass
     note: str = ""
+    kv_heads: Optional[int] = None  # key/value heads (grouped-query); None -> H
+
+    @property
+    def Hkv(self) -> int:
+        return self.H if self.kv_heads is None else self.kv_heads
 
     @property
     def Tp(self) -> int:
@@ -120,6 +128,19 @@ _add(
         B=2, H=4, T=129, D=64, frozen=(1, 3), dtype="bf16", seed=1342,
         qkv_scale=1.0, r_kind="linear_noise", r_slope=0.05, r_noise=0.5,
         prior_len=192,
+    ),
+)
+
+# Qwen3-4B attention layer, grouped-query prefill (forward only): 32 query
+# heads over 8 key/value heads; 30% of the query heads frozen (the last ten,
+# so two key/value groups are entirely frozen and one partly).
+_add(
+    "qwen3_4b_prefill_B4_T4096_30pct",
+    Config(
+        name="qwen3-4b-prefill_B4_H32_KV8_T4096_d128_bf16_30pct-frozen",
+        B=4, H=32, T=4096, D=128, frozen=tuple(range(22, 32)), dtype="bf16",
+        seed=1343, qkv_scale=1.0, r_kind="linear_noise", r_slope=0.02,
+        r_noise=0.5, bwd=False, kv_heads=8,
     ),
 )
 

@@ -1,8 +1,9 @@
 """Seeded generation of Q, K, V, dO, a and r.
 
 The generator is numpy's PCG64 (``default_rng(seed)``).  Draw order is fixed:
-Q, K, V, dO (each a full [B, H, T, D] block of float32 standard normals), then
-a ([H, Tp]), then the noise of r ([H, Tp]).  Rows of ordinary heads are drawn
+Q, K, V, dO (each a full block of float32 standard normals: [B, H, T, D] for
+Q and dO, [B, Hkv, T, D] for K and V), then a ([H, Tp]), then the noise of r
+([H, Tp]).  Rows of ordinary heads are drawn
 too and simply ignored by the layer, so the frozen set can change without
 changing any other value.  Values are scaled, then rounded to the storage
 dtype.  a and r stay float32, as the pages keep their prior buffers in fp32.
@@ -51,8 +52,8 @@ class Inputs:
 
     cfg: Config
     q: np.ndarray  # [B, H, T, D]
-    k: np.ndarray
-    v: np.ndarray
+    k: np.ndarray  # [B, Hkv, T, D]
+    v: np.ndarray  # [B, Hkv, T, D]
     do: Optional[np.ndarray]  # [B, H, T, D] or None for forward-only workloads
     a: np.ndarray  # [H, Tp] float32
     r: np.ndarray  # [H, Tp] float32
@@ -80,9 +81,10 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, with_do: Optional[bool]
     """Draw the inputs of ``cfg`` (seed defaults to ``cfg.seed``)."""
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     shape = (cfg.B, cfg.H, cfg.T, cfg.D)
+    kv_shape = (cfg.B, cfg.Hkv, cfg.T, cfg.D)
     want_do = cfg.bwd if with_do is None else with_do
 
-    def draw():
+    def draw(shape=shape):
         x = rng.standard_normal(shape, dtype=np.float32)
         if cfg.qkv_scale != 1.0:
             x *= np.float32(cfg.qkv_scale)
@@ -93,8 +95,8 @@ def make_inputs(cfg: Config, seed: Optional[int] = None, with_do: Optional[bool]
         return x
 
     q = draw()
-    k = draw()
-    v = draw()
+    k = draw(kv_shape)
+    v = draw(kv_shape)
     do = draw() if want_do else None
     a = rng.standard_normal((cfg.H, cfg.Tp), dtype=np.float32)
     r = _r_vector(cfg, rng)

@@ -466,3 +466,40 @@ def test_pattern_grad_tail_rows_give_tail_entries():
     ta, tr_ = oracle.frozen_rows_pattern_grad(v, do, a, r, np.arange(T0, T))
     np.testing.assert_allclose(ta[T0:], da[T0:], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(tr_[T0:], dr[T0:], rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Grouped-query attention (key/value heads shared by groups of query heads)
+# --------------------------------------------------------------------------
+
+
+def test_gqa_equals_multi_head_with_repeated_kv():
+    B, H, Hk, T, D = 2, 8, 2, 37, 8
+    rng = np.random.default_rng(201)
+    q = rng.standard_normal((B, H, T, D))
+    k, v = rng.standard_normal((B, Hk, T, D)), rng.standard_normal((B, Hk, T, D))
+    a, r = rng.standard_normal((H, T)), rng.standard_normal((H, T))
+    frozen = [0, 1, 0, 0, 1, 1, 1, 1]  # group 1 fully frozen, group 0 mixed
+    O, L = oracle.hybrid_fwd(q, k, v, frozen, a, r)
+    Or, Lr = oracle.hybrid_fwd(q, np.repeat(k, H // Hk, axis=1), np.repeat(v, H // Hk, axis=1), frozen, a, r)
+    np.testing.assert_array_equal(O, Or)
+    np.testing.assert_array_equal(L, Lr)
+    with pytest.raises(ValueError):
+        oracle.hybrid_fwd(q, k[:, :1], v, frozen, a, r)
+    with pytest.raises(ValueError):
+        oracle.hybrid_fwd(q, rng.standard_normal((B, 3, T, D)), rng.standard_normal((B, 3, T, D)), frozen, a, r)
+    with pytest.raises(ValueError):
+        oracle.hybrid_bwd(q, k, v, q, frozen, a, r)
+
+
+def test_gqa_ordinary_equals_sdpa_enable_gqa():
+    B, H, Hk, T, D = 1, 6, 3, 45, 16
+    rng = np.random.default_rng(202)
+    q = rng.standard_normal((B, H, T, D))
+    k, v = rng.standard_normal((B, Hk, T, D)), rng.standard_normal((B, Hk, T, D))
+    a, r = rng.standard_normal((H, T)), rng.standard_normal((H, T))
+    O, _ = oracle.hybrid_fwd(q, k, v, [0] * H, a, r)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), is_causal=True, enable_gqa=True
+    ).numpy()
+    np.testing.assert_allclose(O, ref, rtol=1e-11, atol=1e-12)
