@@ -63,7 +63,7 @@ class SafParams(ctypes.Structure):
         ("frozen", ctypes.POINTER(ctypes.c_uint8)),
         ("stage_events", ctypes.c_void_p),
         ("n_stage_events", ctypes.c_int32),
-        ("reserved1", ctypes.c_int32),
+        ("kv_heads", ctypes.c_int32),
     ]
 
 
@@ -190,7 +190,9 @@ class Params:
     """Owns a SafParams block and the host arrays it points to."""
 
     def __init__(self, v: torch.Tensor, frozen: Sequence[int], prior_len: int,
-                 softmax_scale: Optional[float] = None, events=None):
+                 softmax_scale: Optional[float] = None, events=None, kv_heads: int = 0):
+        """v: any [B, H, T, D] tensor of the call (query heads); kv_heads: key/value
+        heads of a grouped-query call (0: as many as query heads)."""
         B, H, T, D = v.shape
         if len(frozen) != H:
             raise ValueError("frozen mask needs one entry per head")
@@ -202,6 +204,7 @@ class Params:
         self.p.dtype = _dtype_code(v)
         self.p.softmax_scale = 0.0 if softmax_scale is None else float(softmax_scale)
         self.p.frozen = ctypes.cast(self.frozen_arr, ctypes.POINTER(ctypes.c_uint8))
+        self.p.kv_heads = int(kv_heads)
         self.events_arr = None
         if events:
             handles = [int(e.cuda_event) for e in events]
@@ -225,11 +228,21 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
                         workspace=None, stream=None, events=None):
     """Forward of the hybrid layer; returns (O, lse).
 
-    q, k, v: [B, H, T, D] bf16 or fp32 CUDA tensors (unit stride on D);
+    q: [B, H, T, D]; k, v: [B, Hkv, T, D] with Hkv dividing H (grouped-query
+    attention when Hkv < H); bf16 or fp32 CUDA tensors (unit stride on D);
     frozen: length-H sequence of 0/1; a, r: fp32 [H, Tp] contiguous.
     """
-    _check_layer_inputs(v, a, r, q=q, k=k, **({} if out is None else {"out": out}))
-    B, H, T, D = v.shape
+    if not isinstance(k, torch.Tensor) or k.dim() != 4 or q.dim() != 4:
+        raise ValueError("q, k and v must be [B, H, T, D] tensors")
+    if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected (B, Hkv, T, D) matching q {tuple(q.shape)}")
+    Hk = k.shape[1]
+    if Hk < 1 or q.shape[1] % Hk != 0:
+        raise ValueError(f"k and v have {Hk} heads, which must divide the {q.shape[1]} query heads")
+    _check_like("v", v, k)
+    _check_layer_inputs(q, a, r, **({} if out is None else {"out": out}))
+    _check_like("k", k, q, shape=(q.shape[0], Hk) + tuple(q.shape[2:]))
+    B, H, T, D = q.shape
     if out is None:
         out = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
     if lse is None:
@@ -240,7 +253,7 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     if workspace is not None:
         _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
     _require_gpu(v)
-    prm = Params(v, frozen, a.shape[1], softmax_scale, events)
+    prm = Params(q, frozen, a.shape[1], softmax_scale, events, kv_heads=0 if Hk == H else Hk)
     prm.set_strides(q=q, k=k, v=v, o=out)
     ws_n = workspace_bytes(prm, False)
     if workspace is not None:

@@ -31,7 +31,8 @@ bool supported_d(int dtype, int D) {
 int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   if (!p) return SAF_EINVAL;
   if (p->struct_bytes != sizeof(saf_attn_params)) return SAF_EINVAL;
-  if (p->reserved1 != 0) return SAF_EINVAL;
+  if (p->kv_heads < 0 || p->kv_heads > p->H || (p->kv_heads > 0 && p->H % p->kv_heads != 0))
+    return SAF_EINVAL;
   if (p->B < 1 || p->H < 1 || p->T < 1 || p->D < 1) return SAF_EINVAL;
   if (p->T > SAF_MAX_T) return SAF_EUNSUPPORTED;
   if (p->H > SAF_MAX_HEADS) return SAF_EUNSUPPORTED;
@@ -209,6 +210,7 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   args.scale_log2 = resolve_scale(p) * 1.4426950408889634f;
   args.n_ord = n_ord;
   args.n_frz = n_frz;
+  args.kv_group = p->kv_heads > 0 ? p->H / p->kv_heads : 1;
   fill_heads(p, args.ord_heads, args.frz_heads, nullptr);
 
   Stages stg{p, stream};
@@ -255,6 +257,7 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   int n_ord = 0, n_frz = 0;
   int st = check_params(p, &n_ord, &n_frz);
   if (st != SAF_OK) return st;
+  if (p->kv_heads != 0 && p->kv_heads != p->H) return SAF_EUNSUPPORTED;  // grouped-query: forward only
   if (n_ord > 0) {
     if ((st = check_tensor(q, p->q_stride, p)) != SAF_OK) return st;
     if ((st = check_tensor(k, p->k_stride, p)) != SAF_OK) return st;
@@ -331,6 +334,7 @@ int saf_pattern_grad(const saf_attn_params* p, const void* v, const void* o, con
   int n_ord = 0, n_frz = 0;
   int st = check_params(p, &n_ord, &n_frz);
   if (st != SAF_OK) return st;
+  if (p->kv_heads != 0 && p->kv_heads != p->H) return SAF_EUNSUPPORTED;  // grouped-query: forward only
   if ((st = check_tensor(v, p->v_stride, p)) != SAF_OK) return st;
   if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
   if ((st = check_tensor(dout, p->do_stride, p)) != SAF_OK) return st;

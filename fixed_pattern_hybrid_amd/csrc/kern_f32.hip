@@ -49,6 +49,7 @@ template <int D>
 __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
   const int bh = blockIdx.y;
   const int b = bh / A.H, h = bh - b * A.H;
+  const int hk = h / A.kv_group;  // key/value head of this query head
   const int i = blockIdx.x * kRowsPerBlock + threadIdx.x;
   const int T = A.T;
   if (i >= T) return;
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
     const float z2 = A.lse[((int64_t)b * A.H + h) * T + i] * kLog2e;
     for (int j = 0; j <= i; ++j) {
       const float wv = fast_exp2((arow[j] + rrow[i - j]) * kLog2e - z2);
-      const float* vr = rowp(A.v, b, h, j);
+      const float* vr = rowp(A.v, b, hk, j);
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = fmaf(wv, vr[d], acc[d]);
     }
@@ -73,12 +74,12 @@ __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
   float q[D];
   load_row<D>(q, rowp(A.q, b, h, i));
   float m = kNegInf;
-  for (int j = 0; j <= i; ++j) m = fmaxf(m, dot_row<D>(q, rowp(A.k, b, h, j)) * A.scale_log2);
+  for (int j = 0; j <= i; ++j) m = fmaxf(m, dot_row<D>(q, rowp(A.k, b, hk, j)) * A.scale_log2);
   float lsum = 0.f;
   for (int j = 0; j <= i; ++j) {
-    const float p = fast_exp2(dot_row<D>(q, rowp(A.k, b, h, j)) * A.scale_log2 - m);
+    const float p = fast_exp2(dot_row<D>(q, rowp(A.k, b, hk, j)) * A.scale_log2 - m);
     lsum += p;
-    const float* vr = rowp(A.v, b, h, j);
+    const float* vr = rowp(A.v, b, hk, j);
 #pragma unroll
     for (int d = 0; d < D; ++d) acc[d] = fmaf(p, vr[d], acc[d]);
   }

@@ -82,9 +82,10 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
   const int i = q0 + 32 * w + (l & 31);  // this lane's query
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
+  const int hk = h / A.kv_group;  // key/value head of this query head
   const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
-  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
-  const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)hk * A.k.sh;
+  const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)hk * A.v.sh;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[i][16ks + 8*hl + 0..7].
   bf16x8 qf[C::NKS];
@@ -293,7 +294,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
       const int b = b0 + (gb < nb ? gb : 0);
-      const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
+      const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)(h / A.kv_group) * A.v.sh;
       vdma.issue(vg, A.v.st, j0, T, smem + (buf * GL + gb) * C::TILE);
     }
     av.load(arow, j0, T);

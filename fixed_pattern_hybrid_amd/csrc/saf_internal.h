@@ -39,6 +39,7 @@ struct FwdArgs {
   int B, H, T, prior_len;
   float scale_log2;  // softmax_scale * log2(e)
   int n_ord, n_frz;  // number of ordinary / frozen heads
+  int kv_group;      // query heads per key/value head (1: multi-head)
   int frz_group;     // batch elements per frozen program
   int n_groups;      // ceil(B / frz_group)
   int nqb;           // number of query blocks

@@ -24,7 +24,8 @@
  *  - All tensor pointers are DEVICE pointers owned by the caller.  The
  *    library never allocates device memory; scratch space is passed in as a
  *    workspace sized by saf_hybrid_attn_workspace_bytes().
- *  - Q, K, V, O, dO, dQ, dK, dV have logical shape [B][H][T][D].  Their
+ *  - Q, K, V, O, dO, dQ, dK, dV have logical shape [B][H][T][D] (K and V:
+ *    [B][Hkv][T][D] with grouped-query attention, see kv_heads).  Their
  *    element strides for (b, h, t) are given per tensor; the stride of the
  *    last (d) dimension must be 1.  Base pointers must be 16-byte aligned
  *    and each (b, h, t) stride a multiple of 16 bytes.  The t stride may
@@ -107,7 +108,13 @@ typedef struct saf_attn_params {
    * kernels beyond n-1 are not bracketed.  Nothing is skipped or changed. */
   hipEvent_t* stage_events;
   int32_t n_stage_events;
-  int32_t reserved1;        /* must be 0 */
+  /* Key/value heads Hkv (grouped-query attention, the pages' Qwen path in
+   * Appendix D.2): query head h reads key/value head h / (H / Hkv).  0 means
+   * H (multi-head attention).  Otherwise 1 <= Hkv <= H and Hkv divides H; K
+   * and V are then [B][Hkv][T][D] (their h strides step over key/value
+   * heads).  Grouped-query layouts are supported by saf_hybrid_attn_fwd only
+   * (prefill); the backward and saf_pattern_grad return SAF_EUNSUPPORTED. */
+  int32_t kv_heads;
 } saf_attn_params;
 
 /*

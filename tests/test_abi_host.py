@@ -90,7 +90,9 @@ FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on thes
         ({"D": 80}, -2),
         ({"dtype": 5}, -2),
         ({"prior_len": 8}, -1),
-        ({"reserved1": 1}, -1),
+        ({"kv_heads": 3}, -1),
+        ({"kv_heads": -1}, -1),
+        ({"kv_heads": 8}, -1),
         ({"softmax_scale": float("nan")}, -1),
     ],
 )
@@ -269,3 +271,37 @@ def test_binding_pattern_grad_checks(b):
         b.saf_pattern_grad(v, o, do, lse, fz, a, r, dr=mk(H, T, dt=torch.float64))
     with pytest.raises(ValueError, match="GPU"):
         b.saf_pattern_grad(v, o, do, lse, fz, a, r)
+
+
+def test_grouped_query_params(b):
+    # kv_heads divides H: accepted by the forward (rejected here only by the
+    # misaligned lse pointer), refused by the backward and the pattern
+    # gradients (grouped-query layouts are a prefill path)
+    p, arr = _params(b, B=2, H=8, T=64, frozen=[0, 0, 0, 1, 0, 0, 1, 1])
+    p.kv_heads = 2
+    args = [FAKE] * 6
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE + 2, FAKE, 1 << 20, None) == -1
+    assert b.LIB.saf_hybrid_attn_bwd(ctypes.byref(p), *([FAKE] * 11), FAKE, 1 << 20, None) == -2
+    assert b.LIB.saf_pattern_grad(ctypes.byref(p), *([FAKE] * 8), FAKE, 1 << 20, None) == -2
+    p.kv_heads = 8  # = H: multi-head; rejected only by the misaligned lse pointer
+    bargs = [FAKE] * 11
+    bargs[5] = FAKE + 2
+    assert b.LIB.saf_hybrid_attn_bwd(ctypes.byref(p), *bargs, FAKE, 1 << 20, None) == -1
+
+
+def test_binding_grouped_query_checks(b):
+    import torch
+
+    B_, H, Hk, T, D = 2, 8, 2, 16, 64
+    mk = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)  # noqa: E731
+    q, k, v = mk(B_, H, T, D), mk(B_, Hk, T, D), mk(B_, Hk, T, D)
+    a, r = mk(H, T, dt=torch.float32), mk(H, T, dt=torch.float32)
+    fz = [0] * H
+    with pytest.raises(ValueError, match="divide"):
+        b.saf_hybrid_attn_fwd(q, mk(B_, 3, T, D), mk(B_, 3, T, D), fz, a, r)
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_hybrid_attn_fwd(q, k, mk(B_, Hk * 2, T, D), fz, a, r)
+    with pytest.raises(ValueError, match="a and r"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a[:Hk], r[:Hk])
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r)

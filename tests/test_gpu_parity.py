@@ -357,3 +357,87 @@ def test_workload_prefill_32k_sampled_rows(B):
     e = max_abs(host(L[0, h])[rows], rl)
     say(f"  h{h} log N on {len(rows)} rows max-abs {e:.3e}")
     assert e <= LSE_FRZ_ABS
+
+
+# --------------------------------------------------------------------------
+# Grouped-query forward (key/value heads shared by groups of query heads)
+# --------------------------------------------------------------------------
+
+
+def run_gqa_fwd_parity(B, cfg, strided=False):
+    say(f"case {cfg.name} B={cfg.B} H={cfg.H} Hkv={cfg.Hkv} T={cfg.T} D={cfg.D} frozen={cfg.frozen} "
+        f"{cfg.dtype} strided={strided}")
+    inp = make_inputs(cfg, with_do=False)
+    dev = upload(inp)
+    q, k, v = dev["q"], dev["k"], dev["v"]
+    if strided:
+        k = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+        v = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(q, k, v, fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.hybrid_fwd(inp.q, inp.k, inp.v, fz, inp.a, inp.r)
+    for h in range(cfg.H):
+        _check_head(f"h{h}", cfg, host(O[:, h]), ref_o[:, h], host(L[:, h]), ref_l[:, h], fz[h])
+
+
+@pytest.mark.parametrize("Hkv,mask", [(2, (1, 4, 5, 6, 7)), (2, ()), (2, tuple(range(8))), (1, (0, 3)),
+                                      (4, (2, 3)), (8, (5,))])
+def test_gqa_forward_groups_and_masks(B, Hkv, mask):
+    cfg = CONFIGS["pages_check_t129"].with_(H=8, kv_heads=Hkv, B=3, T=300, prior_len=None, frozen=mask,
+                                            bwd=False, name=f"gqa_kv{Hkv}_mask{len(mask)}")
+    run_gqa_fwd_parity(B, cfg)
+
+
+@pytest.mark.parametrize("D", [64, 96, 128])
+def test_gqa_forward_head_dims(B, D):
+    cfg = CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, D=D, B=2, T=257, prior_len=None, frozen=(3, 6),
+                                            bwd=False, qkv_scale=0.5, name=f"gqa_D{D}")
+    run_gqa_fwd_parity(B, cfg)
+
+
+def test_gqa_forward_fp32_and_strided(B):
+    run_gqa_fwd_parity(B, CONFIGS["tiny"].with_(H=8, kv_heads=4, T=70, B=2, frozen=(1, 6), bwd=False,
+                                               name="gqa_fp32"))
+    run_gqa_fwd_parity(B, CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, B=2, T=200, prior_len=None,
+                                                            frozen=(0, 5), bwd=False, name="gqa_strided"),
+                       strided=True)
+
+
+def test_gqa_rejected_by_backward(B):
+    cfg = CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, B=1, T=64, prior_len=None, frozen=(1,),
+                                            name="gqa_bwd")
+    inp = make_inputs(cfg, with_do=True)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    prm = B.Params(dev["q"], fz, dev["a"].shape[1], kv_heads=2)
+    prm.set_strides(q=dev["q"], k=dev["k"], v=dev["v"], o=O, do=dev["do"], dq=O, dk=O, dv=O)
+    ws = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    st = B.LIB.saf_hybrid_attn_bwd(prm.ref(), dev["q"].data_ptr(), dev["k"].data_ptr(), dev["v"].data_ptr(),
+                                   O.data_ptr(), dev["do"].data_ptr(), L.data_ptr(), dev["a"].data_ptr(),
+                                   dev["r"].data_ptr(), O.data_ptr(), O.data_ptr(), O.data_ptr(),
+                                   ws.data_ptr(), ws.numel(), None)
+    assert st == B.SAF_EUNSUPPORTED
+
+
+def test_workload_qwen3_gqa_prefill_sampled_heads(B):
+    cfg = CONFIGS["qwen3_4b_prefill_B4_T4096_30pct"]
+    say(f"workload {cfg.name}")
+    inp = make_inputs(cfg)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(O.float()).all()) and bool(torch.isfinite(L).all())
+    g = cfg.H // cfg.Hkv
+    s = 1.0 / np.sqrt(cfg.D)
+    # an ordinary head and a frozen head of the partly frozen group 5, and a
+    # head of a fully frozen group
+    for b, h in ((3, 20), (0, 23), (2, 31), (1, 0)):
+        say(f"  head b={b} h={h} (kv head {h // g}) frozen={fz[h]}")
+        if fz[h]:
+            ro, rl = oracle.frozen_head_fwd(inp.v[b, h // g], inp.a[h], inp.r[h])
+        else:
+            ro, rl = oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h // g], inp.v[b, h // g], s)
+        _check_head(f"b{b}h{h}", cfg, host(O[b, h]), ro, host(L[b, h]), rl, fz[h])
