@@ -202,6 +202,57 @@ def trainable_pattern_leg(B, cfg, t, stream, reps: int = 20):
                     "step after the layer's backward; not included in value"}
 
 
+# Attention-operation prefill speedups the pages print for the Qwen3-4B
+# grouped-query path over all-ordinary attention (Table 26, in parentheses),
+# keyed by (B, T, replaced fraction in percent).
+PAGES_GQA_SPEEDUP = {
+    (4, 2048, 10): 1.16, (4, 2048, 20): 1.18, (4, 2048, 30): 1.21, (4, 2048, 50): 1.29, (4, 2048, 75): 1.38,
+    (4, 4096, 10): 1.16, (4, 4096, 20): 1.19, (4, 4096, 30): 1.23, (4, 4096, 50): 1.28, (4, 4096, 75): 1.38,
+    (4, 8192, 10): 1.15, (4, 8192, 20): 1.19, (4, 8192, 30): 1.23, (4, 8192, 50): 1.30, (4, 8192, 75): 1.37,
+    (8, 2048, 10): 1.15, (8, 2048, 20): 1.17, (8, 2048, 30): 1.21, (8, 2048, 50): 1.28, (8, 2048, 75): 1.37,
+    (8, 4096, 10): 1.15, (8, 4096, 20): 1.19, (8, 4096, 30): 1.18, (8, 4096, 50): 1.27, (8, 4096, 75): 1.37,
+    (8, 8192, 10): 1.15, (8, 8192, 20): 1.18, (8, 8192, 30): 1.22, (8, 8192, 50): 1.30, (8, 8192, 75): 1.40,
+}
+
+
+def fwd_speedup_vs_ordinary(B, cfg, q, k, v, a, r, fz, reps: int = 10):
+    """Forward time with every head ordinary over the time with the workload's
+    frozen heads, same inputs and shape, timed in A-B-B-A order."""
+    import numpy as np
+    import torch
+
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    kinds = {"ordinary": [0] * cfg.H, "hybrid": fz}
+
+    def run(f):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            B.saf_hybrid_attn_fwd(q, k, v, f, a, r, out=o, lse=lse)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for f in kinds.values():
+        run(f)
+    samples = {n: [] for n in kinds}
+    for order in (("ordinary", "hybrid"), ("hybrid", "ordinary")) * 2:
+        for n in order:
+            samples[n].append(run(kinds[n]))
+    t_o = float(np.median(samples["ordinary"]))
+    t_h = float(np.median(samples["hybrid"]))
+    frac = 100.0 * len(cfg.frozen) / cfg.H
+    col = min((10, 20, 30, 50, 75), key=lambda c: abs(c - frac))  # the pages' nearest column
+    return {"ordinary_ms": round(t_o, 4), "hybrid_ms": round(t_h, 4), "speedup": round(t_o / t_h, 3),
+            "replaced_percent": round(frac, 1),
+            "pages_speedup": PAGES_GQA_SPEEDUP.get((cfg.B, cfg.T, col)) if cfg.Hkv != cfg.H else None,
+            "pages_column_percent": col,
+            "note": "forward of the same shape with every head ordinary vs with the workload's frozen heads; "
+                    "pages_speedup: the attention-operation speedup the pages print for this B, T and "
+                    "fraction (a different machine and baseline kernel; context only)"}
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     """Time the float64 oracle on whole heads of the workload (host cores)."""
     import numpy as np
@@ -216,6 +267,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
         threads = os.cpu_count() or 1
     s = 1.0 / np.sqrt(cfg.D)
     fz = [int(x) for x in inp.frozen]
+    g = cfg.H // cfg.Hkv  # query heads per key/value head
     # alternate ordinary / frozen heads, batch element by batch element, until
     # the budget is used
     ords = [h for h in range(cfg.H) if not fz[h]]
@@ -231,12 +283,12 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     t0 = time.perf_counter()
     for b, h in order:
         if fz[h]:
-            oracle.frozen_head_fwd(inp.v[b, h], inp.a[h], inp.r[h])
+            oracle.frozen_head_fwd(inp.v[b, h // g], inp.a[h], inp.r[h])
             if inp.do is not None:
                 oracle.frozen_head_bwd(inp.do[b, h], inp.a[h], inp.r[h])
             done_frz += 1
         else:
-            oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], s)
+            oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h // g], inp.v[b, h // g], s)
             if inp.do is not None:
                 oracle.ordinary_head_bwd(inp.q[b, h], inp.k[b, h], inp.v[b, h], inp.do[b, h], s)
             done_ord += 1
@@ -264,7 +316,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG,
                     help="workload (synth.CONFIGS key); the default is the headline metric's; others: "
-                         "gpt2_124m_4k_50pct_interleaved, 1b_8k_rank_share, prefill_32k, pages_check_t129, tiny")
+                         "gpt2_124m_4k_50pct_interleaved, 1b_8k_rank_share, prefill_32k, qwen3_4b_prefill_B4_T4096_30pct, "
+                         "pages_check_t129, tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-per-head", action="store_true")
@@ -297,10 +350,10 @@ def main():
     a, r = torch.from_numpy(inp.a).cuda(), torch.from_numpy(inp.r).cuda()
     fz = [int(x) for x in inp.frozen]
     Bn, H, T, D = cfg.B, cfg.H, cfg.T, cfg.D
-    o = torch.empty_like(v)
+    o = torch.empty_like(q)
     lse = torch.empty((Bn, H, T), dtype=torch.float32, device="cuda")
-    dq, dk, dv = torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)
-    prm = B.Params(v, fz, a.shape[1])
+    dq, dk, dv = (torch.empty_like(v), torch.empty_like(v), torch.empty_like(v)) if do is not None else (None,) * 3
+    prm = B.Params(q, fz, a.shape[1], kv_heads=0 if cfg.Hkv == H else cfg.Hkv)
     ws = torch.empty(max(B.workspace_bytes(prm, True), B.workspace_bytes(prm, False), 256),
                      dtype=torch.uint8, device="cuda")
     has_frz = any(fz)
@@ -385,7 +438,8 @@ def main():
         "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name, "B": Bn, "H": H, "T": T, "D": D, "frozen_heads": list(cfg.frozen),
-                   "pass": "fwd+bwd" if do is not None else "fwd"},
+                   "pass": "fwd+bwd" if do is not None else "fwd",
+                   **({"kv_heads": cfg.Hkv} if cfg.Hkv != H else {})},
         "mfma_util": round(value / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(tokens, 1),
         "kernel_ms": {n: round(x, 4) for n, x in kern_ms.items()},
@@ -398,6 +452,8 @@ def main():
         out["trainable_pattern"] = tp
     if not args.no_per_head and do is not None:
         out["per_head"] = per_head_costs(B, cfg)
+    if not args.no_per_head and do is None and has_frz:
+        out["attention_op_speedup"] = fwd_speedup_vs_ordinary(B, cfg, q, k, v, a, r, fz)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)
