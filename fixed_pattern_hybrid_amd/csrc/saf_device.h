@@ -95,14 +95,40 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 lo, bf16x4 hi) {
 
 // Row-major [rows][D] bf16 tile in LDS with rows padded by 16 bytes
 // (pitch D + 8 elements).  Measured on gfx950, this keeps 16-byte fragment
-// reads of 32 consecutive rows near the LDS read rate (about 170 B/clk/CU,
-// against 110 for an XOR-swizzled unpadded tile) and serves the transposing
-// reads at about 110 B/clk/CU.
+// reads of 32 consecutive rows near the LDS read rate (about 170 B/clk/CU)
+// and serves the transposing reads at about 110 B/clk/CU (two-way bank
+// conflicts).  NG: 16-byte chunks per row (the last one is padding).
 template <int D>
 struct LdsLayout {
   static constexpr int PITCH = D + 8;  // elements per row
+  static constexpr int NG = PITCH / 8;
   // element offset of (row, col)
   __device__ static __forceinline__ int off(int row, int col) { return row * PITCH + col; }
+  // global chunk held at chunk position pos of a row (pos = D/8 is padding)
+  __device__ static __forceinline__ int chunk(int row, int pos) { return pos; }
+};
+
+// Row-major [rows][D] bf16 tile without padding for D = 64 and 128: chunk c
+// of row r sits at chunk position c ^ swz(r).  With 64 banks of 4 bytes, both
+// fragment reads touch every bank once per pass: 16 lanes reading one chunk
+// of 16 consecutive rows, and 32 lanes reading 4 consecutive chunks of 4
+// consecutive rows (the transposing read), which the padded layout serves
+// with two-way conflicts.  The lane offsets cost registers (a chunk position
+// per fragment), so it is used where those are available.  Other D: padded.
+template <int D>
+struct SwzLayout {
+  static constexpr bool SWZ = D == 64 || D == 128;
+  static constexpr int PITCH = SWZ ? D : D + 8;
+  static constexpr int NG = PITCH / 8;
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 64) return ((row >> 1) & 3) | ((((row >> 1) ^ (row >> 3)) & 1) << 2);
+    else if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+    else return 0;
+  }
+  __device__ static __forceinline__ int off(int row, int col) {
+    return row * PITCH + ((((col >> 3) ^ swz(row))) << 3) + (col & 7);
+  }
+  __device__ static __forceinline__ int chunk(int row, int pos) { return pos ^ swz(row); }
 };
 
 // MFMA operand whose k index runs along rows of a row-major LDS tile X.
@@ -112,9 +138,8 @@ struct LdsLayout {
 // i.e. slot e of half h maps to row row0 + 8*(e/4) + 4*h + e%4 -- exactly the
 // row labelling of the C registers 8*(s%2)..8*(s%2)+7 of a 32x32 accumulator
 // block, so a C block converted with pack_acc8 pairs with this operand.
-template <int D>
+template <int D, class L = LdsLayout<D>>
 __device__ __forceinline__ bf16x8 lds_frag_tr(const lds_bf16* X, int row0, int col0) {
-  using L = LdsLayout<D>;
   const int l = lane_id();
   const int g = l >> 4;        // 16-lane group
   const int s16 = l & 15;
@@ -128,10 +153,10 @@ __device__ __forceinline__ bf16x8 lds_frag_tr(const lds_bf16* X, int row0, int c
 
 // MFMA operand whose k index runs along columns of a row-major LDS tile:
 // lane l receives X[row0 + l%32][col0 + 8*(l/32) + e], e = 0..7.
-template <int D>
+template <int D, class L = LdsLayout<D>>
 __device__ __forceinline__ bf16x8 lds_frag_nat(const lds_bf16* X, int row0, int col0) {
   const int l = lane_id();
-  return lds_read8(X, LdsLayout<D>::off(row0 + (l & 31), col0 + 8 * (l >> 5)));
+  return lds_read8(X, L::off(row0 + (l & 31), col0 + 8 * (l >> 5)));
 }
 
 // Exchange with the lane 32 positions away (the other half of a C column).

@@ -67,22 +67,22 @@ struct BandStage {
 
 // A [ROWS][D] bf16 tile copied from global memory straight into LDS (buffer
 // loads with the LDS modifier; no registers, no LDS store instructions), in
-// the padded LdsLayout<D> arrangement.  One wave-wide load writes 64
-// consecutive 16-byte granules of LDS (lane l at granule l); a padded row is
-// D/8 + 1 granules, so lane l of load m fetches granule g = 64 m + l, i.e.
-// row g / (D/8 + 1), chunk g % (D/8 + 1); the pad granule and rows >= T take
-// an offset outside the buffer range and are written as zeros.  The four
-// waves of the block share the loads (wave w issues loads w, w+4, ...).
+// the arrangement of layout L (padded LdsLayout<D> by default).  One
+// wave-wide load writes 64 consecutive 16-byte granules of LDS (lane l at
+// granule l); a row is L::NG granules, so lane l of load m fills granule
+// g = 64 m + l, i.e. row g / NG, position g % NG, with the global chunk the
+// layout keeps there; a pad granule and rows >= T take an offset outside the
+// buffer range and are written as zeros.  The four waves of the block share
+// the loads (wave w issues loads w, w+4, ...).
 // The data is visible to the block after s_waitcnt vmcnt(0) in every wave
 // and a barrier.
-template <int D, int ROWS, bool KEEP = true>
+template <int D, int ROWS, bool KEEP = true, class L = LdsLayout<D>>
 struct TileDma {
-  static constexpr int NG = D / 8 + 1;       // granules per padded row
+  static constexpr int NG = L::NG;           // granules per row
   static constexpr int NI = ROWS * NG / 64;  // wave-wide loads per tile
   static constexpr int PER = (NI + 3) / 4;   // loads per wave (4 waves)
   static constexpr int kOob = 0x7ffffff0;    // beyond any buffer range used here
   static_assert(ROWS * NG % 64 == 0, "tile must be whole wave-wide loads");
-  static_assert(LdsLayout<D>::PITCH * 2 == NG * 16, "padded row is D/8 + 1 granules");
   // Per-lane byte offsets of this wave's loads: kept in registers (KEEP) or
   // recomputed at each issue where registers are scarcer.
   static constexpr bool kKeep = KEEP;
@@ -92,8 +92,8 @@ struct TileDma {
   __device__ __forceinline__ int offset(int k) const {
     const int m = __builtin_amdgcn_readfirstlane(wave_id()) + 4 * k;
     const int g = 64 * m + lane_id();
-    const int row = g / NG, col = g - row * NG;
-    return (m >= NI || col == NG - 1) ? kOob : row * ste * 2 + col * 16;
+    const int row = g / NG, pos = g - row * NG;
+    return (m >= NI || pos >= D / 8) ? kOob : row * ste * 2 + L::chunk(row, pos) * 16;
   }
 
   // st: row stride of the tensor (elements, at most SAF_MAX_T_STRIDE)
