@@ -64,6 +64,7 @@ class SafParams(ctypes.Structure):
         ("stage_events", ctypes.c_void_p),
         ("n_stage_events", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
+        ("logz", ctypes.c_void_p),
     ]
 
 
@@ -225,12 +226,15 @@ def workspace_bytes(params: Params, for_bwd: bool) -> int:
 
 
 def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse=None,
-                        workspace=None, stream=None, events=None):
+                        workspace=None, stream=None, events=None, logz=None):
     """Forward of the hybrid layer; returns (O, lse).
 
     q: [B, H, T, D]; k, v: [B, Hkv, T, D] with Hkv dividing H (grouped-query
     attention when Hkv < H); bf16 or fp32 CUDA tensors (unit stride on D);
     frozen: length-H sequence of 0/1; a, r: fp32 [H, Tp] contiguous.
+    logz: optional fp32 [H, T] precomputed log N of the frozen heads (as
+    saf_pattern_lognorm(a, r, T) returns it); the call then skips the
+    normaliser computation and copies it into lse.
     """
     if not isinstance(k, torch.Tensor) or k.dim() != 4 or q.dim() != 4:
         raise ValueError("q, k and v must be [B, H, T, D] tensors")
@@ -252,9 +256,14 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
         raise ValueError("lse must be contiguous float32 [B, H, T]")
     if workspace is not None:
         _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
+    if logz is not None:
+        _check_like("logz", logz, q, shape=(H, T), dtype=torch.float32)
+        if not logz.is_contiguous():
+            raise ValueError("logz must be contiguous float32 [H, T]")
     _require_gpu(v)
     prm = Params(q, frozen, a.shape[1], softmax_scale, events, kv_heads=0 if Hk == H else Hk)
     prm.set_strides(q=q, k=k, v=v, o=out)
+    prm.p.logz = _ptr(logz)
     ws_n = workspace_bytes(prm, False)
     if workspace is not None:
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()

@@ -99,7 +99,7 @@ size_t bwd_ws_bytes(const saf_attn_params* p) {
 // (frozen head, key group, row), at most 32 groups.  The fp32 forward needs
 // none.
 size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
-  if (p->dtype != SAF_BF16 || n_frz == 0) return 0;
+  if (p->dtype != SAF_BF16 || n_frz == 0 || p->logz) return 0;
   return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
 }
 
@@ -191,6 +191,7 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
   if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
   if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
+  if (p->logz && !aligned(p->logz, 4)) return SAF_EINVAL;
   const size_t need = fwd_ws_bytes(p, n_frz);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return SAF_EWORKSPACE;
 
@@ -213,9 +214,11 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   args.kv_group = p->kv_heads > 0 ? p->H / p->kv_heads : 1;
   fill_heads(p, args.ord_heads, args.frz_heads, nullptr);
 
+  args.logz = p->logz;
+
   Stages stg{p, stream};
   if (stg.mark() != hipSuccess) return SAF_EHIP;
-  if (n_frz > 0) {
+  if (n_frz > 0 && !p->logz) {
     LognormArgs la;
     std::memset(&la, 0, sizeof(la));
     la.a = a;

@@ -60,7 +60,9 @@ __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
   if (head_is_frozen(A.frz_heads, A.n_frz, h)) {
     const float* arow = A.a + (int64_t)h * A.prior_len;
     const float* rrow = A.r + (int64_t)h * A.prior_len;
-    const float z2 = A.lse[((int64_t)b * A.H + h) * T + i] * kLog2e;
+    float* lrow = A.lse + ((int64_t)b * A.H + h) * T;
+    if (A.logz) lrow[i] = A.logz[(int64_t)h * T + i];  // the caller's precomputed log N
+    const float z2 = lrow[i] * kLog2e;
     for (int j = 0; j <= i; ++j) {
       const float wv = fast_exp2((arow[j] + rrow[i - j]) * kLog2e - z2);
       const float* vr = rowp(A.v, b, hk, j);

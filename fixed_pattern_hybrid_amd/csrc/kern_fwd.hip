@@ -261,7 +261,11 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   // log N(i) in log2 units: merge the key-group partials of this row, and
   // record it as the row's lse for every batch element of the group.
   float z2 = 0.f;
-  if (i < T) {
+  if (i < T && A.logz) {
+    z2 = A.logz[(int64_t)h * T + i] * kLog2e;  // the caller's precomputed log N
+    if (hl == 0)
+      for (int gb = 0; gb < nb; ++gb) A.lse[((int64_t)(b0 + gb) * A.H + h) * T + i] = A.logz[(int64_t)h * T + i];
+  } else if (i < T) {
     float M = kNegInf, S = 0.f;
     const float2* part = A.lz_part + (int64_t)hidx * A.lz_ngroups * T + i;
     const int cmax = i / A.lz_group;  // groups 0..cmax hold this row's terms

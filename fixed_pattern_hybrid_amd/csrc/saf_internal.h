@@ -48,6 +48,8 @@ struct FwdArgs {
   // and write lse.
   const float2* lz_part;
   int lz_group, lz_ngroups;
+  // precomputed log N [H][T] (natural log) of the caller, or null
+  const float* logz;
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
 };

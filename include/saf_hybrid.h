@@ -115,6 +115,16 @@ typedef struct saf_attn_params {
    * heads).  Grouped-query layouts are supported by saf_hybrid_attn_fwd only
    * (prefill); the backward and saf_pattern_grad return SAF_EUNSUPPORTED. */
   int32_t kv_heads;
+  /* Optional precomputed row normalisers of the frozen heads (the log Z the
+   * paper stores with alpha and rho, Section 3.3 and Appendix D.2): a DEVICE
+   * fp32 array [H][T], row h = log N of head h over rows 0..T-1, as
+   * saf_pattern_lognorm writes it for the rows of a and r (rows of ordinary
+   * heads are not read).  When non-NULL, saf_hybrid_attn_fwd reads it instead
+   * of computing the normalisers (no normaliser kernel, no workspace) and
+   * copies it into the frozen rows of lse; it must be the normaliser of the
+   * a and r passed, which the library does not check.  NULL: computed by the
+   * call.  Read by saf_hybrid_attn_fwd only. */
+  const float* logz;
 } saf_attn_params;
 
 /*
@@ -134,7 +144,8 @@ typedef struct saf_attn_params {
  *             needs none.
  *             Contents on entry are ignored and left undefined on return.
  * Kernels: the frozen heads' row normalisers (bf16: chunk partials, merged
- * by the frozen programs of the next launch), then one mixed-head launch.
+ * by the frozen programs of the next launch; skipped when p->logz is given),
+ * then one mixed-head launch.
  */
 int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k,
                         const void* v, const float* a, const float* r, void* o,
@@ -154,7 +165,8 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k,
                         void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                         hipStream_t stream);
 
-/* Workspace bytes a call with these parameters needs (0 if none);
+/* Workspace bytes a call with these parameters needs (0 if none; the
+ * forward needs none when p->logz is given);
  * for_bwd = 0 for the forward, 1 for the backward.  Returns 0 for invalid p. */
 size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd);
 

@@ -43,16 +43,18 @@ def test_param_block_layout_matches_c(tmp_path, b):
     src = tmp_path / "sz.c"
     src.write_text(
         '#include <stdio.h>\n#include <stddef.h>\n#include "saf_hybrid.h"\n'
-        "int main(void){printf(\"%zu %zu %zu %zu %zu\\n\", sizeof(saf_attn_params),"
+        "int main(void){printf(\"%zu %zu %zu %zu %zu %zu %zu\\n\", sizeof(saf_attn_params),"
         " offsetof(saf_attn_params, q_stride), offsetof(saf_attn_params, dv_stride),"
-        " offsetof(saf_attn_params, frozen), offsetof(saf_attn_params, n_stage_events));return 0;}\n"
+        " offsetof(saf_attn_params, frozen), offsetof(saf_attn_params, n_stage_events),"
+        " offsetof(saf_attn_params, kv_heads), offsetof(saf_attn_params, logz));return 0;}\n"
     )
     exe = tmp_path / "sz"
     subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include", f"-I{ROOT}/include",
                     str(src), "-o", str(exe)], check=True)
     got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True).stdout.split()]
     P = b.SafParams
-    want = [ctypes.sizeof(P), P.q_stride.offset, P.dv_stride.offset, P.frozen.offset, P.n_stage_events.offset]
+    want = [ctypes.sizeof(P), P.q_stride.offset, P.dv_stride.offset, P.frozen.offset, P.n_stage_events.offset,
+            P.kv_heads.offset, P.logz.offset]
     assert got == want
 
 
@@ -165,6 +167,11 @@ def test_fwd_workspace_checks(b):
     assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE + 16, need, None) == -3
     p32, arr32 = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1], dtype=b.SAF_F32)
     assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p32), 0) == 0
+    p.logz = FAKE  # precomputed normalisers: no partials
+    assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0) == 0
+    p.logz = FAKE + 2
+    assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE, need, None) == -1
+    p.logz = None
     pord, arro = _params(b, B=2, H=4, T=T)
     assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(pord), 0) == 0
 

@@ -441,3 +441,37 @@ def test_workload_qwen3_gqa_prefill_sampled_heads(B):
         else:
             ro, rl = oracle.ordinary_head_fwd(inp.q[b, h], inp.k[b, h // g], inp.v[b, h // g], s)
         _check_head(f"b{b}h{h}", cfg, host(O[b, h]), ro, host(L[b, h]), rl, fz[h])
+
+
+# --------------------------------------------------------------------------
+# Precomputed normalisers (the stored log Z of the frozen heads)
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("key,kv", [("pages_check_t129", None), ("tiny", None), ("pages_check_t129", 2)])
+def test_forward_with_precomputed_lognorm(B, key, kv):
+    cfg = CONFIGS[key].with_(T=300 if key != "tiny" else 128, prior_len=None, B=2, H=8,
+                             frozen=(1, 2, 6), name=f"logz_{key}_kv{kv}", kv_heads=kv, bwd=kv is None)
+    say(f"case {cfg.name} dtype={cfg.dtype}")
+    inp = make_inputs(cfg, with_do=kv is None)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    logz = B.saf_pattern_lognorm(dev["a"], dev["r"], cfg.T)  # [H, T]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"], logz=logz)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.hybrid_fwd(inp.q, inp.k, inp.v, fz, inp.a, inp.r)
+    for h in range(cfg.H):
+        _check_head(f"h{h}", cfg, host(O[:, h]), ref_o[:, h], host(L[:, h]), ref_l[:, h], fz[h])
+        if fz[h]:
+            for b in range(cfg.B):
+                assert torch.equal(L[b, h], logz[h]), "frozen lse rows are the given log N"
+    if kv is None:
+        # the backward reads the copied normalisers from lse
+        dq, dk, dv = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"])
+        torch.cuda.synchronize()
+        ref_dq, ref_dk, ref_dv = oracle.hybrid_bwd(inp.q, inp.k, inp.v, inp.do, fz, inp.a, inp.r)
+        bar = _bars(cfg)["g_rel"]
+        for n, g, rr in (("dQ", dq, ref_dq), ("dK", dk, ref_dk), ("dV", dv, ref_dv)):
+            e = rel_l2(host(g), rr)
+            say(f"  {n} rel-L2 {e:.3e}")
+            assert e <= bar, (n, e)
