@@ -290,10 +290,26 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   const int last_key = min(q0 + kBM, T) - 1;
   const int ntiles = last_key / kBN + 1;
 
+  // Factored weights: W[i][j] = ea[j] er[i-j] f_i with ea = 2^(a2[j] - ca),
+  // er = 2^(r2[d] - cr) (both <= 1; ca, cr the maxima over the block's keys
+  // and offsets) and f_i = 2^(ca + cr - z2_i), which scales the output row:
+  // one multiply per weight instead of an exponential.  Every row of the
+  // block must have f_i <= 2^90 (terms that underflow are then below 2^-36
+  // of their row); otherwise (a and r whose ranges are far apart) the block
+  // takes the exponential per weight.
+  float ca = kNegInf, cr = kNegInf;
+  for (int x = threadIdx.x; x <= last_key; x += kThreads) {
+    ca = fmaxf(ca, arow[x]);
+    cr = fmaxf(cr, rrow[x]);  // offsets 0 .. last_key are the block's
+  }
+  ca = block_max(ca, fbase) * kLog2e;
+  cr = block_max(cr, fbase) * kLog2e;
+  const bool exact = __syncthreads_or(i < T && !(ca + cr - z2 <= 90.f));
+
   // Next-tile operands, loaded into registers at the start of a tile and
   // written to LDS at its end: the V tiles of the group, a (log2 units) of
   // the tile keys (-inf for keys >= T) and the r band over the offsets of the
-  // tile, band[x] = r2[q0 - j0 - (BN-1) + x].
+  // tile, band[x] = r2[q0 - j0 - (BN-1) + x] (factored: ea and er).
   TileDma<D, kBN, true, typename C::L> vdma;
   vdma.init(A.v.st);
   ScalarStage av;
@@ -310,8 +326,13 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   };
   auto store_next = [&](int buf) {
     lds_f32* as = fbase + buf * FSTRIDE;
-    if (threadIdx.x < kBN) as[threadIdx.x] = av.valid ? av.v * kLog2e : kNegInf;
-    band.store(as + kBN);
+    if (exact) {
+      if (threadIdx.x < kBN) as[threadIdx.x] = av.valid ? av.v * kLog2e : kNegInf;
+      band.store(as + kBN);
+    } else {
+      if (threadIdx.x < kBN) as[threadIdx.x] = av.valid ? fast_exp2(av.v * kLog2e - ca) : 0.f;
+      band.store_exp(as + kBN, cr);
+    }
     wait_vm_loads();
   };
 
@@ -325,6 +346,8 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) oacc[gb][db] = f32x16{};
 
+  auto tiles = [&](auto exact_tag) {
+  constexpr bool EXACT = decltype(exact_tag)::value;
   for (int t = 0; t < ntiles; ++t) {
     const int j0 = t * kBN;
     const bool more = (t + 1) < ntiles;
@@ -348,7 +371,8 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
           const f32x4 a4 = lds_read_f4(as + base);
           const f32x4 r4 = lds_read_f4(rc + (xi - base - 3));  // band[y0 .. y0+3]
 #pragma unroll
-          for (int k = 0; k < 4; ++k) wv[4 * hh + k] = fast_exp2(a4[k] + r4[3 - k] - z2);
+          for (int k = 0; k < 4; ++k)
+            wv[4 * hh + k] = EXACT ? fast_exp2(a4[k] + r4[3 - k] - z2) : a4[k] * r4[3 - k];
         }
         const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
 #pragma unroll
@@ -362,10 +386,14 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
     if (more) store_next(buf ^ 1);
     __syncthreads();
   }
+  };
+  if (exact) tiles(std::true_type{});
+  else tiles(std::false_type{});
 
+  const float f_i = exact ? 1.f : fast_exp2(ca + cr - z2);
 #pragma unroll
   for (int gb = 0; gb < G; ++gb)
-    if (gb < nb) store_out_rows<D>(A.o, b0 + gb, h, i, T, oacc[gb], 1.f);
+    if (gb < nb) store_out_rows<D>(A.o, b0 + gb, h, i, T, oacc[gb], f_i);
 }
 
 // One launch for every head: program p -> (query block rank, slot); each

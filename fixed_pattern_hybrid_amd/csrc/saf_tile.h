@@ -63,7 +63,31 @@ struct BandStage {
       }
     }
   }
+  // The same copies holding 2^(log2(e) r - shift) (0 outside [0, T)).
+  __device__ __forceinline__ void store_exp(lds_f32* rs, float shift) const {
+    const int x = threadIdx.x;
+    if (x < BAND + 3) {
+      const float val = valid ? fast_exp2(v * kLog2e - shift) : 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int y = x - c;
+        if (y >= 0 && y < BAND) rs[c * STRIDE + y] = val;
+      }
+    }
+  }
 };
+
+// Maximum of x over the block (every thread gets it); scratch: 4 floats of
+// LDS, free until the barrier this makes.
+__device__ __forceinline__ float block_max(float x, lds_f32* scratch) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  if ((threadIdx.x & 63) == 0) scratch[threadIdx.x >> 6] = x;
+  __syncthreads();
+  x = fmaxf(fmaxf(scratch[0], scratch[1]), fmaxf(scratch[2], scratch[3]));
+  __syncthreads();
+  return x;
+}
 
 // A [ROWS][D] bf16 tile copied from global memory straight into LDS (buffer
 // loads with the LDS modifier; no registers, no LDS store instructions), in
