@@ -475,3 +475,30 @@ def test_forward_with_precomputed_lognorm(B, key, kv):
             e = rel_l2(host(g), rr)
             say(f"  {n} rel-L2 {e:.3e}")
             assert e <= bar, (n, e)
+
+
+@pytest.mark.parametrize("spike", [60.0, 70.0])
+def test_frozen_wide_range_patterns(B, spike):
+    # a and r spiking at unrelated positions (a[0] = r[5] = spike): in log2
+    # units the sum of their maxima exceeds the normaliser of rows like i = 1
+    # by about spike * log2(e) -- 87 (factored weights, close to their 90
+    # limit) or 101 (beyond it: those blocks take the per-weight
+    # exponential).  Both must match the oracle.
+    cfg = CONFIGS["pages_check_t129"].with_(T=400, prior_len=None, B=3, name=f"wide_range_{spike:g}")
+    inp = make_inputs(cfg, with_do=True)
+    for h in (1, 3):
+        inp.a[h, 0] = spike
+        inp.r[h, 5] = spike
+        inp.a[h, 200] = -40.0
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    dq, dk, dv = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.hybrid_fwd(inp.q, inp.k, inp.v, fz, inp.a, inp.r)
+    ref_dv = oracle.hybrid_bwd(inp.q, inp.k, inp.v, inp.do, fz, inp.a, inp.r)[2]
+    for h in (1, 3):
+        _check_head(f"h{h}", cfg, host(O[:, h]), ref_o[:, h], host(L[:, h]), ref_l[:, h], True)
+        e = rel_l2(host(dv[:, h]), ref_dv[:, h])
+        say(f"  h{h} dV rel-L2 {e:.3e}")
+        assert e <= BF16_GRAD_RELL2
