@@ -33,6 +33,10 @@ EXPORTED = (
     "saf_pattern_grad",
     "saf_pattern_grad_workspace_bytes",
     "saf_pattern_lognorm",
+    "saf_fit_targets",
+    "saf_fit_targets_workspace_bytes",
+    "saf_fit_pattern",
+    "saf_fit_pattern_workspace_bytes",
     "saf_status_string",
     "saf_version",
 )
@@ -97,6 +101,16 @@ def _load():
     lib.saf_pattern_dense.restype = ctypes.c_int
     lib.saf_pattern_lognorm.argtypes = [i32, i32, i32, vp, vp, vp, vp]
     lib.saf_pattern_lognorm.restype = ctypes.c_int
+    f32, i64 = ctypes.c_float, ctypes.c_int64
+    lib.saf_fit_targets.argtypes = [i32, i32, vp, i64, i64, f32, vp, vp, vp, vp, sz, vp]
+    lib.saf_fit_targets.restype = ctypes.c_int
+    lib.saf_fit_targets_workspace_bytes.argtypes = [i32, i32]
+    lib.saf_fit_targets_workspace_bytes.restype = sz
+    lib.saf_fit_pattern.argtypes = [i32, i32, vp, vp, vp, i32, f32, f32, f32, f32,
+                                    vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.saf_fit_pattern.restype = ctypes.c_int
+    lib.saf_fit_pattern_workspace_bytes.argtypes = [i32, i32]
+    lib.saf_fit_pattern_workspace_bytes.restype = sz
     lib.saf_status_string.argtypes = [ctypes.c_int]
     lib.saf_status_string.restype = ctypes.c_char_p
     lib.saf_version.argtypes = []
@@ -365,4 +379,85 @@ def saf_pattern_lognorm(a: torch.Tensor, r: torch.Tensor, T: int, stream=None) -
     out = torch.empty((n, T), dtype=torch.float32, device=a.device)
     _check(LIB.saf_pattern_lognorm(n, T, Tp, _ptr(a), _ptr(r), _ptr(out), _stream_handle(stream)),
            "saf_pattern_lognorm")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Compact-pattern fitting.
+# ---------------------------------------------------------------------------
+
+FIT_FLOOR = 1e-9   # target floor of the pages' recipe
+FIT_STEPS = 400    # Adam steps of the pages' recipe
+FIT_LR = 0.05      # Adam learning rate of the pages' recipe
+
+
+def fit_targets_workspace_bytes(n_heads: int, T: int) -> int:
+    return int(LIB.saf_fit_targets_workspace_bytes(int(n_heads), int(T)))
+
+
+def fit_pattern_workspace_bytes(n_heads: int, T: int) -> int:
+    return int(LIB.saf_fit_pattern_workspace_bytes(int(n_heads), int(T)))
+
+
+def _fit_vec(name: str, t: torch.Tensor, shape, device) -> None:
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous float32 {tuple(shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.dtype != torch.uint8 or workspace.numel() < nbytes or workspace.device != device:
+        raise ValueError(f"workspace must be uint8 with at least {nbytes} bytes on {device}")
+    return workspace
+
+
+def saf_fit_targets(ahat: torch.Tensor, floor: float = FIT_FLOOR, workspace=None, stream=None):
+    """Sufficient statistics of calibration means ``ahat`` (fp32 [n, T, T]
+    or [T, T], last dimension contiguous): returns (eta_abs [n, T],
+    eta_rel [n, T], negent [n])."""
+    if ahat.dtype != torch.float32 or ahat.dim() not in (2, 3) or not ahat.is_cuda:
+        raise ValueError("ahat must be a float32 [n, T, T] or [T, T] GPU tensor")
+    a3 = ahat if ahat.dim() == 3 else ahat.unsqueeze(0)
+    n, T, T2 = a3.shape
+    if T != T2 or a3.stride(2) != 1:
+        raise ValueError("ahat must be square with a contiguous last dimension")
+    dev = a3.device
+    eta_abs = torch.empty((n, T), dtype=torch.float32, device=dev)
+    eta_rel = torch.empty((n, T), dtype=torch.float32, device=dev)
+    negent = torch.empty((n,), dtype=torch.float32, device=dev)
+    nbytes = fit_targets_workspace_bytes(n, T)
+    ws = _workspace(nbytes, dev, workspace)
+    head_stride = a3.stride(0) if n > 1 else 0
+    _check(LIB.saf_fit_targets(n, T, _ptr(a3), head_stride, a3.stride(1), float(floor),
+                               _ptr(eta_abs), _ptr(eta_rel), _ptr(negent), _ptr(ws), ws.numel(),
+                               _stream_handle(stream)), "saf_fit_targets")
+    return eta_abs, eta_rel, negent
+
+
+def saf_fit_pattern(eta_abs: torch.Tensor, eta_rel: torch.Tensor, negent: Optional[torch.Tensor] = None,
+                    steps: int = FIT_STEPS, lr: float = FIT_LR, betas=(0.9, 0.999), eps: float = 1e-8,
+                    workspace=None, stream=None):
+    """Fit compact patterns to target marginals ([n, T] each): returns a dict
+    with a, r, logz ([n, T]) and loss, kappa ([n]; kappa only when negent
+    is given)."""
+    if eta_abs.dim() != 2 or not eta_abs.is_cuda:
+        raise ValueError("eta_abs must be a float32 [n, T] GPU tensor")
+    n, T = eta_abs.shape
+    dev = eta_abs.device
+    _fit_vec("eta_abs", eta_abs, (n, T), dev)
+    _fit_vec("eta_rel", eta_rel, (n, T), dev)
+    if negent is not None:
+        _fit_vec("negent", negent, (n,), dev)
+    out = {k: torch.empty((n, T), dtype=torch.float32, device=dev) for k in ("a", "r", "logz")}
+    out["loss"] = torch.empty((n,), dtype=torch.float32, device=dev)
+    out["kappa"] = torch.empty((n,), dtype=torch.float32, device=dev) if negent is not None else None
+    nbytes = fit_pattern_workspace_bytes(n, T)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(LIB.saf_fit_pattern(n, T, _ptr(eta_abs), _ptr(eta_rel), _ptr(negent), int(steps), float(lr),
+                               float(betas[0]), float(betas[1]), float(eps), _ptr(out["a"]), _ptr(out["r"]),
+                               _ptr(out["logz"]), _ptr(out["loss"]), _ptr(out["kappa"]), _ptr(ws),
+                               ws.numel(), _stream_handle(stream)), "saf_fit_pattern")
     return out

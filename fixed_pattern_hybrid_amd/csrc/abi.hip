@@ -418,4 +418,139 @@ int saf_pattern_lognorm(int32_t n_heads, int32_t T, int32_t prior_len, const flo
   return saf::launch_lognorm_identity(la, stream) == hipSuccess ? SAF_OK : SAF_EHIP;
 }
 
+namespace {
+
+bool fit_sizes_ok(int32_t n_heads, int32_t T) {
+  return n_heads >= 1 && n_heads <= SAF_MAX_FIT_HEADS && T >= 1 && T <= SAF_MAX_T;
+}
+
+size_t fit_targets_ws(int32_t n_heads, int32_t T) {
+  const size_t nT = (size_t)n_heads * (size_t)T;
+  const size_t nseg = ((size_t)T + saf::kFitSegRows - 1) / saf::kFitSegRows;
+  return 2 * round_up(nT * sizeof(float), 256) + round_up(nT * 2 * nseg * sizeof(float), 256);
+}
+
+size_t fit_pattern_ws(int32_t n_heads, int32_t T) {
+  return 6 * round_up((size_t)n_heads * (size_t)T * sizeof(float), 256);
+}
+
+}  // namespace
+
+size_t saf_fit_targets_workspace_bytes(int32_t n_heads, int32_t T) {
+  return fit_sizes_ok(n_heads, T) ? fit_targets_ws(n_heads, T) : 0;
+}
+
+int saf_fit_targets(int32_t n_heads, int32_t T, const float* ahat, int64_t head_stride,
+                    int64_t row_stride, float floor, float* eta_abs, float* eta_rel, float* negent,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!fit_sizes_ok(n_heads, T)) return SAF_EINVAL;
+  if (!(floor > 0.f) || !std::isfinite(floor)) return SAF_EINVAL;
+  if (!ahat || !aligned(ahat, 4) || row_stride < T || head_stride < 0) return SAF_EINVAL;
+  if (!eta_abs || !eta_rel || !negent || !aligned(eta_abs, 4) || !aligned(eta_rel, 4) ||
+      !aligned(negent, 4))
+    return SAF_EINVAL;
+  const size_t need = fit_targets_ws(n_heads, T);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return SAF_EWORKSPACE;
+  const size_t nT = (size_t)n_heads * (size_t)T;
+  char* w = static_cast<char*>(ws);
+  saf::FitTargetArgs ta;
+  std::memset(&ta, 0, sizeof(ta));
+  ta.ahat = ahat;
+  ta.head_stride = head_stride;
+  ta.row_stride = row_stride;
+  ta.floor = floor;
+  ta.n_heads = n_heads;
+  ta.T = T;
+  ta.nseg = (T + saf::kFitSegRows - 1) / saf::kFitSegRows;
+  ta.inv_s = reinterpret_cast<float*>(w);
+  ta.row_ent = reinterpret_cast<float*>(w + round_up(nT * sizeof(float), 256));
+  ta.part = reinterpret_cast<float*>(w + 2 * round_up(nT * sizeof(float), 256));
+  ta.eta_abs = eta_abs;
+  ta.eta_rel = eta_rel;
+  ta.negent = negent;
+  return saf::launch_fit_targets(ta, stream) == hipSuccess ? SAF_OK : SAF_EHIP;
+}
+
+size_t saf_fit_pattern_workspace_bytes(int32_t n_heads, int32_t T) {
+  return fit_sizes_ok(n_heads, T) ? fit_pattern_ws(n_heads, T) : 0;
+}
+
+int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const float* eta_rel,
+                    const float* negent, int32_t steps, float lr, float beta1, float beta2, float eps,
+                    float* a, float* r, float* logz, float* loss, float* kappa, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  if (!fit_sizes_ok(n_heads, T) || steps < 0) return SAF_EINVAL;
+  if (!(lr > 0.f) || !std::isfinite(lr) || !(beta1 >= 0.f && beta1 < 1.f) ||
+      !(beta2 >= 0.f && beta2 < 1.f) || !(eps > 0.f) || !std::isfinite(eps))
+    return SAF_EINVAL;
+  const float* in[] = {eta_abs, eta_rel, a, r, logz};
+  for (const float* x : in)
+    if (!x || !aligned(x, 4)) return SAF_EINVAL;
+  if ((negent && !aligned(negent, 4)) || (loss && !aligned(loss, 4)) || (kappa && !aligned(kappa, 4)))
+    return SAF_EINVAL;
+  if (kappa && !negent) return SAF_EINVAL;
+  const size_t need = fit_pattern_ws(n_heads, T);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return SAF_EWORKSPACE;
+  const size_t vec = round_up((size_t)n_heads * (size_t)T * sizeof(float), 256);
+  char* w = static_cast<char*>(ws);
+  float* pa[2] = {a, reinterpret_cast<float*>(w)};
+  float* pr[2] = {r, reinterpret_cast<float*>(w + vec)};
+
+  saf::FitStepArgs fa;
+  std::memset(&fa, 0, sizeof(fa));
+  fa.eta_abs = eta_abs;
+  fa.eta_rel = eta_rel;
+  fa.logz = logz;
+  fa.m_a = reinterpret_cast<float*>(w + 2 * vec);
+  fa.v_a = reinterpret_cast<float*>(w + 3 * vec);
+  fa.m_r = reinterpret_cast<float*>(w + 4 * vec);
+  fa.v_r = reinterpret_cast<float*>(w + 5 * vec);
+  fa.n_heads = n_heads;
+  fa.T = T;
+  fa.beta1 = beta1;
+  fa.beta2 = beta2;
+  fa.eps = eps;
+
+  LognormArgs la;
+  std::memset(&la, 0, sizeof(la));
+  la.out = logz;
+  la.out_b_stride = 0;
+  la.out_h_stride = T;
+  la.n_heads = n_heads;
+  la.B = 1;
+  la.T = T;
+  la.prior_len = T;
+
+  // step t reads buffer (t - 1 + s0) & 1 and writes (t + s0) & 1, so the
+  // last step lands in the caller's a and r
+  const int s0 = steps & 1;
+  fa.a_next = pa[s0];
+  fa.r_next = pr[s0];
+  if (saf::launch_fit_init(fa, stream) != hipSuccess) return SAF_EHIP;
+  for (int t = 1; t <= steps; ++t) {
+    const int cur = (t - 1 + s0) & 1, nxt = (t + s0) & 1;
+    la.a = pa[cur];
+    la.r = pr[cur];
+    if (saf::launch_lognorm_identity(la, stream) != hipSuccess) return SAF_EHIP;
+    fa.a_cur = pa[cur];
+    fa.r_cur = pr[cur];
+    fa.a_next = pa[nxt];
+    fa.r_next = pr[nxt];
+    const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
+    const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
+    fa.lr_bc1 = (float)((double)lr / bc1);
+    fa.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+    if (saf::launch_fit_step(fa, stream) != hipSuccess) return SAF_EHIP;
+  }
+  la.a = a;
+  la.r = r;
+  if (saf::launch_lognorm_identity(la, stream) != hipSuccess) return SAF_EHIP;
+  if (loss || kappa) {
+    fa.a_cur = a;
+    fa.r_cur = r;
+    if (saf::launch_fit_loss(fa, negent, loss, kappa, stream) != hipSuccess) return SAF_EHIP;
+  }
+  return SAF_OK;
+}
+
 }  // extern "C"

@@ -135,6 +135,48 @@ constexpr int kPgradBN = 128;    // keys per bf16 program
 constexpr int kPgradQC = 512;    // queries per bf16 program
 constexpr int kPgradDiag = 640;  // offsets per program: kPgradQC + kPgradBN - 1, padded
 
+// Compact-pattern fitting: target statistics of calibration means.
+struct FitTargetArgs {
+  const float* ahat;    // [n][T] rows of row_stride floats, heads head_stride apart
+  int64_t head_stride, row_stride;
+  float floor;          // causal entries are floored at this value
+  int n_heads, T, nseg;
+  float* inv_s;         // workspace [n][T]: 1 / row sum of the floored entries
+  float* row_ent;       // workspace [n][T]: sum_j p log p of each row
+  float* part;          // workspace [n][2][nseg][T]: segment partial marginals
+  float* eta_abs;       // [n][T] output
+  float* eta_rel;       // [n][T] output
+  float* negent;        // [n] output
+};
+
+// One Adam step of the fit (also the initialisation and the final loss).
+struct FitStepArgs {
+  const float* eta_abs;  // [n][T]
+  const float* eta_rel;  // [n][T]
+  const float* a_cur;    // [n][T] parameters at the current point
+  const float* r_cur;
+  const float* logz;     // [n][T] log N at the current point (natural log)
+  float* a_next;         // [n][T] updated parameters
+  float* r_next;
+  float* m_a;            // [n][T] Adam moments
+  float* v_a;
+  float* m_r;
+  float* v_r;
+  int n_heads, T;
+  float beta1, beta2, eps;
+  float lr_bc1;          // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
+};
+
+constexpr int kFitSegRows = 512;       // rows per partial of the target marginals
+constexpr float kFitInitFloor = 1e-9f;  // floor inside the initial r
+
+hipError_t launch_fit_targets(const FitTargetArgs& args, hipStream_t stream);
+hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream);
+hipError_t launch_fit_step(const FitStepArgs& args, hipStream_t stream);
+hipError_t launch_fit_loss(const FitStepArgs& args, const float* negent, float* loss, float* kappa,
+                           hipStream_t stream);
+
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program
 constexpr int kBwdKvBN = 128;   // keys per key-block program

@@ -224,6 +224,82 @@ int saf_pattern_lognorm(int32_t n_heads, int32_t T, int32_t prior_len,
                         const float* a, const float* r, float* logz,
                         hipStream_t stream);
 
+/*
+ * Compact-pattern fitting ("When Can Attention Heads Be Statically
+ * Defined?": Algorithm 1, which prepares a target from a head's calibration
+ * mean, fits a and r, and accepts the fit by its row-averaged KL divergence;
+ * Section 3.2 "Fitting", Equation 4; Appendix A.2 "Selection, fitting, and
+ * installation"; Appendix D.1, Equation 20).
+ */
+#define SAF_MAX_FIT_HEADS 16384
+
+/*
+ * Target statistics of n_heads calibration means A (fp32 [T][T] each, the
+ * average causal attention of one head; entries above the diagonal are never
+ * read).  With P[i][j] = max(A[i][j], floor) / sum_{k<=i} max(A[i][k], floor)
+ * for j <= i (the floored, row-normalised target):
+ *   eta_abs[h][j] = sum_{i>=j} P[i][j]        (column sums, 0 <= j < T)
+ *   eta_rel[h][d] = sum_{i>=d} P[i][i-d]      (diagonal sums, 0 <= d < T)
+ *   negent[h]     = sum_i sum_{j<=i} P[i][j] ln P[i][j]
+ * the sufficient statistics of the fit and of its acceptance test.
+ *   ahat        : device fp32; row i of head h starts at
+ *                 ahat + h * head_stride + i * row_stride (elements);
+ *                 4-byte aligned, row_stride >= T, head_stride >= 0.  Rows
+ *                 that start 16-byte aligned are read 16 bytes at a time.
+ *   floor       : > 0 and finite (the pages floor at 1e-9).
+ *   eta_abs, eta_rel : device fp32 [n_heads][T] outputs.
+ *   negent      : device fp32 [n_heads] output.
+ *   ws          : saf_fit_targets_workspace_bytes(n_heads, T) bytes,
+ *                 256-byte aligned: row sums and entropies, and partial
+ *                 marginals over row segments, summed in a fixed order
+ *                 (results are bitwise deterministic).
+ * Each row is accumulated in fp32; negent sums the rows in fp64.
+ * n_heads in [1, SAF_MAX_FIT_HEADS], T in [1, SAF_MAX_T].
+ */
+int saf_fit_targets(int32_t n_heads, int32_t T, const float* ahat, int64_t head_stride,
+                    int64_t row_stride, float floor, float* eta_abs, float* eta_rel,
+                    float* negent, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes saf_fit_targets needs (0 for invalid sizes). */
+size_t saf_fit_targets_workspace_bytes(int32_t n_heads, int32_t T);
+
+/*
+ * Fit one compact pattern per head to target marginals.  Each head starts
+ * from a = 0 and r[d] = ln max(eta_rel[d] / (T - d), 1e-9) and takes `steps`
+ * Adam steps (Kingma & Ba: moment decays beta1 and beta2, bias-corrected
+ * moments, eps added to the square root of the second moment; the pages use
+ * 400 steps at lr 0.05 with no early stopping) on Equation 4,
+ *   L(a, r) = (1/T) [ sum_i ln N(i) - sum_j eta_abs[j] a[j]
+ *                     - sum_d eta_rel[d] r[d] ],
+ *   N(i) = sum_{k<=i} exp(a[k] + r[i-k]),
+ * whose gradient is (fitted marginal - target marginal) / T for both
+ * vectors (Equation 20); a and r are updated from the gradient at the same
+ * point.
+ *   eta_abs, eta_rel : device fp32 [n_heads][T] (saf_fit_targets).
+ *   negent      : device fp32 [n_heads] or NULL; needed for kappa.
+ *   a, r        : device fp32 [n_heads][T] outputs: the fitted parameters.
+ *   logz        : device fp32 [n_heads][T] output: ln N(i) of the fitted
+ *                 pattern (saf_attn_params.logz takes it, in [H][T] rows).
+ *   loss        : device fp32 [n_heads] output or NULL: L at the result.
+ *   kappa       : device fp32 [n_heads] output or NULL: negent / T + L,
+ *                 the row-averaged KL divergence of the fitted pattern from
+ *                 the target (the pages accept a fit when kappa <= 0.2 nats;
+ *                 the decision is the caller's).
+ *   ws          : saf_fit_pattern_workspace_bytes(n_heads, T) bytes,
+ *                 256-byte aligned: a second parameter buffer and the four
+ *                 Adam moment vectors.
+ * steps >= 0; lr > 0; beta1, beta2 in [0, 1); eps > 0; all finite.
+ * Arithmetic is fp32 (loss and kappa are summed in fp64).  Two kernels are
+ * launched per step; on SAF_EHIP the outputs are unspecified.
+ */
+int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const float* eta_rel,
+                    const float* negent, int32_t steps, float lr, float beta1, float beta2,
+                    float eps, float* a, float* r, float* logz, float* loss, float* kappa,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes saf_fit_pattern needs (0 for invalid sizes). */
+size_t saf_fit_pattern_workspace_bytes(int32_t n_heads, int32_t T);
+
 /* Static description of a status code (never NULL). */
 const char* saf_status_string(int status);
 

@@ -9,9 +9,10 @@ multiplicative noise that no compact pattern reproduces exactly.
 
 For head ``head`` of a target set with seed ``seed`` the generator is numpy's
 PCG64 seeded with [seed, head], so any head can be regenerated alone.  Draw
-order: the head's shape parameters (sink, decay, noise level, zero fraction),
-then a [T, T] block of standard normals (noise), then a [T, T] block of
-uniforms (zeroed entries).  Weights are
+order: the head's shape parameters (sink, decay, noise level, zero
+fraction), then T(T+1)/2 standard normals (noise) and T(T+1)/2 uniforms
+(zeroed entries), each over the causal entries (i, j <= i) in row-major
+order.  Weights are
 
     w[i, j] = (1 + i - j) ** (-decay) * (1 + sink * [j == 0]) * exp(noise * n[i, j])
 
@@ -48,16 +49,18 @@ def calibration_mean(T: int, seed: int, head: int, spec: TargetSpec = DEFAULT_SP
     decay = rng.uniform(*spec.decay)
     noise = rng.uniform(*spec.noise)
     zero_frac = rng.uniform(*spec.zero_frac)
-    n = rng.standard_normal((T, T))
-    u = rng.random((T, T))
-    i = np.arange(T)[:, None]
-    j = np.arange(T)[None, :]
-    causal = j <= i
-    dist = np.where(causal, i - j, 0).astype(np.float64)
-    w = (1.0 + dist) ** (-decay) * np.where(j == 0, 1.0 + sink, 1.0) * np.exp(noise * n)
-    w = np.where(causal & ((u >= zero_frac) | (i == j)), w, 0.0)
-    w /= w.sum(axis=1, keepdims=True)
-    return w.astype(np.float32)
+    decay_by_dist = (1.0 + np.arange(T, dtype=np.float64)) ** (-decay)
+    ii, jj = np.tril_indices(T)  # causal entries, row-major
+    n = rng.standard_normal(ii.size)
+    u = rng.random(ii.size)
+    w = decay_by_dist[ii - jj] * np.exp(noise * n)
+    w[jj == 0] *= 1.0 + sink
+    w[(u < zero_frac) & (ii != jj)] = 0.0
+    starts = ii.searchsorted(np.arange(T))  # first entry of each row
+    w /= np.add.reduceat(w, starts)[ii]
+    out = np.zeros((T, T), dtype=np.float32)
+    out[ii, jj] = w
+    return out
 
 
 def calibration_means(T: int, n_heads: int, seed: int, spec: TargetSpec = DEFAULT_SPEC) -> np.ndarray:
@@ -66,3 +69,21 @@ def calibration_means(T: int, n_heads: int, seed: int, spec: TargetSpec = DEFAUL
     for h in range(n_heads):
         out[h] = calibration_mean(T, seed, h, spec)
     return out
+
+
+@dataclass(frozen=True)
+class FitWorkload:
+    """A set of heads to fit: n_heads calibration means of length T."""
+
+    name: str
+    n_heads: int
+    T: int
+    seed: int
+
+
+# The 124M model at 4K context with 25% of its 12 x 12 heads replaced: 36
+# fits at T = 4096 (the setting of the pages' fitting-cost table, Table 13).
+FIT_WORKLOADS = {
+    "gpt2_124m_25pct": FitWorkload("gpt2-124m-fit_H36_T4096_25pct", 36, 4096, 1337),
+    "small": FitWorkload("fit-small_H4_T300", 4, 300, 7),
+}

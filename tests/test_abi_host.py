@@ -312,3 +312,88 @@ def test_binding_grouped_query_checks(b):
         b.saf_hybrid_attn_fwd(q, k, v, fz, a[:Hk], r[:Hk])
     with pytest.raises(ValueError, match="GPU"):
         b.saf_hybrid_attn_fwd(q, k, v, fz, a, r)
+
+
+def _ru(x, a=256):
+    return -(-x // a) * a
+
+
+def test_fit_workspace_sizes(b):
+    L = b.LIB
+    assert L.saf_fit_targets_workspace_bytes(0, 10) == 0
+    assert L.saf_fit_targets_workspace_bytes(3, 0) == 0
+    assert L.saf_fit_targets_workspace_bytes(16385, 10) == 0
+    # row sums and entropies [n][T], partial marginals [n][2][ceil(T/512)][T]
+    assert L.saf_fit_targets_workspace_bytes(3, 1000) == 2 * _ru(3000 * 4) + _ru(3000 * 2 * 2 * 4)
+    assert L.saf_fit_targets_workspace_bytes(36, 4096) == 2 * _ru(36 * 4096 * 4) + _ru(36 * 4096 * 2 * 8 * 4)
+    # second parameter buffer and four moment vectors, 256-byte aligned each
+    assert L.saf_fit_pattern_workspace_bytes(3, 1000) == 6 * _ru(3000 * 4)
+    assert L.saf_fit_pattern_workspace_bytes(1, 1) == 6 * 256
+    assert L.saf_fit_pattern_workspace_bytes(0, 5) == 0
+    assert L.saf_fit_pattern_workspace_bytes(2, (1 << 20) + 1) == 0
+
+
+def test_fit_targets_rejects_before_launch(b):
+    L = b.LIB
+    n, T = 2, 100
+    need = L.saf_fit_targets_workspace_bytes(n, T)
+    ok = dict(n=n, T=T, ahat=FAKE, hs=T * T, rs=T, floor=1e-9, ea=FAKE, er=FAKE, ne=FAKE, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        x = {**ok, **kw}
+        return L.saf_fit_targets(x["n"], x["T"], x["ahat"], x["hs"], x["rs"], x["floor"], x["ea"], x["er"],
+                                 x["ne"], x["ws"], x["wsb"], None)
+
+    assert call(n=0) == -1
+    assert call(T=0) == -1
+    assert call(floor=0.0) == -1
+    assert call(floor=float("inf")) == -1
+    assert call(floor=float("nan")) == -1
+    assert call(ahat=None) == -1
+    assert call(ahat=FAKE + 2) == -1  # 4-byte alignment
+    assert call(rs=T - 1) == -1
+    assert call(hs=-4) == -1
+    assert call(ea=None) == -1
+    assert call(ne=FAKE + 2) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=need - 1) == -3
+    assert call(ws=FAKE + 16) == -3
+
+
+def test_fit_pattern_rejects_before_launch(b):
+    L = b.LIB
+    n, T = 2, 100
+    need = L.saf_fit_pattern_workspace_bytes(n, T)
+    ok = dict(n=n, T=T, ea=FAKE, er=FAKE, ne=FAKE, steps=400, lr=0.05, b1=0.9, b2=0.999, eps=1e-8,
+              a=FAKE, r=FAKE, z=FAKE, loss=FAKE, kappa=FAKE, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        x = {**ok, **kw}
+        return L.saf_fit_pattern(x["n"], x["T"], x["ea"], x["er"], x["ne"], x["steps"], x["lr"], x["b1"],
+                                 x["b2"], x["eps"], x["a"], x["r"], x["z"], x["loss"], x["kappa"], x["ws"],
+                                 x["wsb"], None)
+
+    assert call(n=0) == -1
+    assert call(T=0) == -1
+    assert call(steps=-1) == -1
+    assert call(lr=0.0) == -1
+    assert call(lr=float("nan")) == -1
+    assert call(b1=1.0) == -1
+    assert call(b2=-0.1) == -1
+    assert call(eps=0.0) == -1
+    assert call(ea=None) == -1
+    assert call(z=FAKE + 1) == -1
+    assert call(ne=None) == -1  # kappa needs negent
+    assert call(loss=FAKE + 2) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=need - 1) == -3
+    assert call(ws=FAKE + 64) == -3
+
+
+def test_fit_binding_checks_without_gpu(b):
+    import torch
+
+    with pytest.raises(ValueError):
+        b.saf_fit_targets(torch.zeros(4, 4))  # not a GPU tensor
+    with pytest.raises(ValueError):
+        b.saf_fit_pattern(torch.zeros(2, 4), torch.zeros(2, 4))
