@@ -431,7 +431,9 @@ size_t fit_targets_ws(int32_t n_heads, int32_t T) {
 }
 
 size_t fit_pattern_ws(int32_t n_heads, int32_t T) {
-  return 6 * round_up((size_t)n_heads * (size_t)T * sizeof(float), 256);
+  const size_t nseg = ((size_t)T + saf::kSegMax - 1) / saf::kSegMax;
+  return 6 * round_up((size_t)n_heads * (size_t)T * sizeof(float), 256) +
+         5 * round_up((size_t)n_heads * nseg * sizeof(float), 256);
 }
 
 }  // namespace
@@ -505,49 +507,48 @@ int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const floa
   fa.v_a = reinterpret_cast<float*>(w + 3 * vec);
   fa.m_r = reinterpret_cast<float*>(w + 4 * vec);
   fa.v_r = reinterpret_cast<float*>(w + 5 * vec);
+  const size_t segv = round_up((size_t)n_heads * (((size_t)T + saf::kSegMax - 1) / saf::kSegMax) * sizeof(float), 256);
+  float* sa[2] = {reinterpret_cast<float*>(w + 6 * vec), reinterpret_cast<float*>(w + 6 * vec + segv)};
+  float* sr[2] = {reinterpret_cast<float*>(w + 6 * vec + 2 * segv), reinterpret_cast<float*>(w + 6 * vec + 3 * segv)};
+  fa.smax_z = reinterpret_cast<float*>(w + 6 * vec + 4 * segv);
   fa.n_heads = n_heads;
   fa.T = T;
+  fa.nseg = (T + saf::kSegMax - 1) / saf::kSegMax;
   fa.beta1 = beta1;
   fa.beta2 = beta2;
   fa.eps = eps;
-
-  LognormArgs la;
-  std::memset(&la, 0, sizeof(la));
-  la.out = logz;
-  la.out_b_stride = 0;
-  la.out_h_stride = T;
-  la.n_heads = n_heads;
-  la.B = 1;
-  la.T = T;
-  la.prior_len = T;
 
   // step t reads buffer (t - 1 + s0) & 1 and writes (t + s0) & 1, so the
   // last step lands in the caller's a and r
   const int s0 = steps & 1;
   fa.a_next = pa[s0];
   fa.r_next = pr[s0];
+  fa.smax_a_next = sa[s0];
+  fa.smax_r_next = sr[s0];
   if (saf::launch_fit_init(fa, stream) != hipSuccess) return SAF_EHIP;
   for (int t = 1; t <= steps; ++t) {
     const int cur = (t - 1 + s0) & 1, nxt = (t + s0) & 1;
-    la.a = pa[cur];
-    la.r = pr[cur];
-    if (saf::launch_lognorm_identity(la, stream) != hipSuccess) return SAF_EHIP;
     fa.a_cur = pa[cur];
     fa.r_cur = pr[cur];
+    fa.smax_a_cur = sa[cur];
+    fa.smax_r_cur = sr[cur];
+    if (saf::launch_fit_norm(fa, logz, stream) != hipSuccess) return SAF_EHIP;
     fa.a_next = pa[nxt];
     fa.r_next = pr[nxt];
+    fa.smax_a_next = sa[nxt];
+    fa.smax_r_next = sr[nxt];
     const double bc1 = 1.0 - std::pow((double)beta1, (double)t);
     const double bc2 = 1.0 - std::pow((double)beta2, (double)t);
     fa.lr_bc1 = (float)((double)lr / bc1);
     fa.inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
     if (saf::launch_fit_step(fa, stream) != hipSuccess) return SAF_EHIP;
   }
-  la.a = a;
-  la.r = r;
-  if (saf::launch_lognorm_identity(la, stream) != hipSuccess) return SAF_EHIP;
+  fa.a_cur = a;
+  fa.r_cur = r;
+  fa.smax_a_cur = sa[0];
+  fa.smax_r_cur = sr[0];
+  if (saf::launch_fit_norm(fa, logz, stream) != hipSuccess) return SAF_EHIP;
   if (loss || kappa) {
-    fa.a_cur = a;
-    fa.r_cur = r;
     if (saf::launch_fit_loss(fa, negent, loss, kappa, stream) != hipSuccess) return SAF_EHIP;
   }
   return SAF_OK;

@@ -16,24 +16,24 @@
 //   fit_tred_kernel   fixed-order sums of the segment partials (eta_abs,
 //                     eta_rel); fit_negent_kernel sums the row entropies.
 //
-// The fit (two launches per Adam step):
-//   the normaliser kernel of the forward writes log N of the current (a, r);
-//   fit_step_kernel computes the fitted marginals
+// The fit (two launches per Adam step), both one band-sum program with
+// 256 outputs per block (four per lane):
+//   fit_norm_kernel  log N(i) of the current (a, r) (Equation 3);
+//   fit_step_kernel  the fitted marginals
 //     mu_abs(k) = exp(a_k) * sum_{i >= k} exp(r_{i-k} - z_i)
 //     mu_rel(d) = exp(r_d) * sum_{k < T-d} exp(a_k - z_{k+d})
-//   for 64 parameters per block (one per lane; kind 0 = a, kind 1 = r), the
-//   gradient (mu - eta) / T (Equation 20) and the Adam update, written to
-//   the other of two parameter buffers so that every block of a step reads
-//   the same point.
+//   (kind 0 = a, kind 1 = r), the gradient (mu - eta) / T (Equation 20) and
+//   the Adam update, written to the other of two parameter buffers so that
+//   every block of a step reads the same point.
 //
-// The marginal sums factor like the normaliser's: over a chunk of kTK
+// The sums factor like the forward's normaliser: over a chunk of kTK
 // summation indices, exp2(X[x] + Y[y]) = 2^(mx + my) exp2(X[x] - mx)
-// exp2(Y[y] - my), where X is indexed by the summation index (kind 0: -log2
-// N of row i; kind 1: log2 e * a_k) and Y by a band index that moves with
-// both the summation index and the lane (kind 0: log2 e * r at offset i - k;
-// kind 1: -log2 N of row k + d).  Each term is one FMA on two staged
-// exponentials (both <= 1); a lane whose chunk sum falls below 2^-20 is
-// recomputed exactly with a max-shifted sum, as in the normaliser.
+// exp2(Y[y] - my), where X is indexed by the summation index and Y by a band
+// index that moves with both the summation index and the output.  Each term
+// is one FMA on two staged exponentials (both <= 1); an output whose chunk
+// sum falls below 2^-96 (where underflowed terms could matter) is recomputed
+// exactly with a max-shifted sum.  The
+// next chunk's staging values are loaded while the current chunk is summed.
 #include "saf_internal.h"
 #include "saf_device.h"
 #include "saf_tile.h"
@@ -168,40 +168,43 @@ __global__ __launch_bounds__(256) void fit_negent_kernel(FitTargetArgs A) {
 // The fit.
 // ---------------------------------------------------------------------------
 
-constexpr int kOut = 64;  // parameters per step block (one per lane)
-constexpr int kWaves = 4;
-constexpr int kNT = kOut * kWaves;
-constexpr int kTK = 256;  // summation indices per chunk
-constexpr int kBand = kOut + kTK - 1;
-constexpr int kBS = band_stride(kBand);
-static_assert(kBand + 3 <= 2 * kNT && kBS % 4 == 0 && kBS >= kBand + 3, "band layout");
+constexpr int kQ = 4;                 // parameters per lane
+#ifndef SAF_FIT_WAVES
+#define SAF_FIT_WAVES 4
+#endif
+constexpr int kWaves = SAF_FIT_WAVES;  // waves per block, splitting each chunk
+constexpr int kNT = 64 * kWaves;
+constexpr int kOut = 64 * kQ;         // parameters per step block
+constexpr int kTK = 256;              // summation indices per chunk
+constexpr int kBand = kOut + kTK - 1; // band entries a chunk touches
+constexpr int kBandPad = kBand + 1;   // one zero entry past the end
+static_assert(kBandPad % 4 == 0, "band rows are read 16 bytes at a time");
+
+struct StageBuf {
+  float x2[kTK];        // X of the chunk (log2 units)
+  float y2[kBandPad];   // Y of the chunk's band (log2 units)
+  __attribute__((aligned(16))) float xe[kTK];      // exp2(X - mx)
+  __attribute__((aligned(16))) float ye[kBandPad]; // exp2(Y - my), 0 past the band
+};
 
 struct StepSmem {
-  float x2[kTK];    // X of the chunk (log2 units)
-  float y2[kBand];  // Y of the chunk's band (log2 units)
-  __attribute__((aligned(16))) float xe[kTK];  // exp2(X - mx)
-  // exp2(Y - my) in four copies: copy c holds band entry y + c at y (0 past
-  // the end), so four consecutive entries starting anywhere are one aligned
-  // 16-byte read
-  __attribute__((aligned(16))) float ye[4 * kBS];
-  float red[8];
+  StageBuf buf[2];  // chunk c uses buf[c & 1]
+  float red[kWaves];
   float cm[kWaves][kOut];
   float cs[kWaves][kOut];
 };
 
-__device__ __forceinline__ void block_max2(float& u, float& v, float* red) {
-  for (int o = 32; o >= 1; o >>= 1) {
-    u = fmaxf(u, __shfl_xor(u, o, 64));
-    v = fmaxf(v, __shfl_xor(v, o, 64));
-  }
+static_assert(kSegMax == kOut && kSegMax == kTK, "segment maxima cover one block's outputs / one chunk");
+
+// Maximum over the block of v; every thread gets it.
+__device__ __forceinline__ float block_max1(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   __syncthreads();
-  if (lane_id() == 0) {
-    red[wave_id()] = u;
-    red[4 + wave_id()] = v;
-  }
+  if (lane_id() == 0) red[wave_id()] = v;
   __syncthreads();
-  u = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  v = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  float m = red[0];
+  for (int x = 1; x < (int)(blockDim.x >> 6); ++x) m = fmaxf(m, red[x]);
+  return m;
 }
 
 __device__ __forceinline__ void lse_merge(float& M, float& S, float cm, float cs) {
@@ -212,145 +215,326 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float cm, float cs
   }
 }
 
-// One block: parameters o0 .. o0+63 of kind KIND for head h.
-//   KIND 0 (a): output k = o0 + lane; chunk rows i = c0 + x;
-//               X[x] = -z2[i], band y = x - lane + (kOut - 1) at offset
-//               i - k = c0 - o0 - (kOut - 1) + y, Y[y] = r2[offset].
-//   KIND 1 (r): output d = o0 + lane; chunk keys k = c0 + x;
-//               X[x] = a2[k], band y = x + lane at row i = c0 + o0 + y,
-//               Y[y] = -z2[i].
-// Entries outside [0, T) are -inf (their exponentials 0).
+// Band-sum programs.  A block owns 256 outputs o0 .. o0+255 of head h; lane
+// L of every wave owns o0 + 4L + q (q = 0..3), and the four waves split
+// each chunk's summation indices in groups of four (x = 4 (w + 4u)).  Per
+// kind, with chunk index n = c0 + x:
+//   KIND 0 (gradient of a, output k): rows i = n, X[x] = -z2[i]; the band
+//     entry of (x, k) is y = x - (k - o0) + (kOut - 1), at offset
+//     i - k = c0 - o0 - (kOut - 1) + y, Y[y] = r2[offset].
+//   KIND 1 (gradient of r, output d): keys k = n, X[x] = a2[k]; band
+//     y = x + (d - o0) at row i = c0 + o0 + y, Y[y] = -z2[i].
+//   KIND 2 (normaliser, output row i): keys k = n, X[x] = a2[k]; band
+//     y = (i - o0) - x + (kTK - 1) at offset i - k = o0 - c0 - (kTK - 1) + y,
+//     Y[y] = r2[offset].
+// So y = SX x + SO (4L + q) + OFF, and the seven entries a lane needs for a
+// group x..x+3 start at yb = SX x + SO 4L + OFFB, a multiple of four: two
+// aligned 16-byte reads for sixteen products.  Entries outside [0, T) are
+// -inf (their exponentials 0).
 template <int KIND>
-__device__ void fit_step_block(const FitStepArgs& A, StepSmem& sm) {
+struct BandKind {
+  static constexpr int SX = KIND == 2 ? -1 : 1;
+  static constexpr int SO = KIND == 0 ? -1 : 1;
+  static constexpr int OFF = KIND == 0 ? kOut - 1 : (KIND == 1 ? 0 : kTK - 1);
+  static constexpr int OFFB = KIND == 0 ? kOut - 4 : (KIND == 1 ? 0 : kTK - 4);
+  // position of entry (q, e) among the seven starting at yb
+  __device__ static constexpr int idx(int q, int e) {
+    return KIND == 0 ? 3 + e - q : (KIND == 1 ? q + e : 3 + q - e);
+  }
+};
+
+// Staging values are loaded raw from a clamped (always valid) index, one
+// chunk ahead and without branches, so the loads stay in flight while the
+// current chunk is summed; band_val turns a raw value into log2 units (-inf
+// where the index falls outside the band or [0, T)).
+template <int KIND>
+__device__ __forceinline__ int band_x_idx(int n, int T, bool& ok) {
+  ok = n < T;
+  return min(n, T - 1);
+}
+
+template <int KIND>
+__device__ __forceinline__ int band_y_idx(int c0, int o0, int y, int T, bool& ok) {
+  const int n = KIND == 1 ? c0 + o0 + y : (KIND == 0 ? c0 - o0 - (kOut - 1) + y : o0 - c0 - (kTK - 1) + y);
+  ok = y < kBand && n >= 0 && n < T;
+  return min(max(n, 0), T - 1);
+}
+
+__device__ __forceinline__ float band_val(float raw, bool ok, bool negate) {
+  return ok ? (negate ? -raw : raw) * kLog2e : kNegInf;
+}
+
+// Exact max-shifted sum of one output's terms over a wave's groups of a
+// chunk (x = g .. g+3 for g = xq, xq + 4 kWaves, ... up to xlast; band index
+// SX x + yq), as a (max, sum) pair in log2 units.  Rarely taken, so kept out
+// of line: the summing loop keeps its registers.
+__device__ __attribute__((noinline)) float2 exact_chunk_sum(const float* x2, const float* y2, int sx, int yq,
+                                                            int xq, int xlast) {
+  float cm = kNegInf;
+  for (int g = xq; g <= xlast; g += 4 * kWaves)
+    for (int x = g; x < g + 4 && x <= xlast; ++x) cm = fmaxf(cm, x2[x] + y2[sx * x + yq]);
+  float cs = 0.f;
+  if (cm != kNegInf)
+    for (int g = xq; g <= xlast; g += 4 * kWaves)
+      for (int x = g; x < g + 4 && x <= xlast; ++x) cs += fast_exp2(x2[x] + y2[sx * x + yq] - cm);
+  return make_float2(cm, cs);
+}
+
+// Whether any of a wave's summation indices (x with x mod 16 in [xq, xq+3],
+// 0 <= x <= xlast) falls in output o's causal range for the chunk at c0:
+//   kind 0 (output k): rows i = c0 + x with k <= i < T;
+//   kind 1 (output d): keys k = c0 + x with 0 <= k < T - d;
+//   kind 2 (output i): keys k = c0 + x with 0 <= k <= i.
+// Terms in that range are finite (a, r and log N are), so a zero sum with
+// no such index is exact and needs no recomputation.
+template <int KIND>
+__device__ __forceinline__ bool wave_has_terms(int o, int c0, int xq, int xlast, int T) {
+  int lo = KIND == 0 ? o - c0 : -c0;
+  int hi = KIND == 0 ? T - 1 - c0 : (KIND == 1 ? T - 1 - o - c0 : o - c0);
+  lo = max(lo, 0);
+  hi = min(hi, xlast);
+  if (lo > hi) return false;
+  const int period = 4 * kWaves;
+  const int r = lo % period;
+  const int first = r < xq ? lo - r + xq : (r <= xq + 3 ? lo : lo - r + period + xq);
+  return first <= hi;
+}
+
+// Sixteen products of one group of four summation indices.
+template <int KIND>
+__device__ __forceinline__ void group_fma(const lds_f32* xe, const lds_f32* ye, int x, int yb, float* s) {
+  using K = BandKind<KIND>;
+  const f32x4 e4 = lds_read_f4(xe + x);
+  const f32x4 ya = lds_read_f4(ye + yb);
+  const f32x4 yc = lds_read_f4(ye + (yb + 4));
+  const float yv[8] = {ya[0], ya[1], ya[2], ya[3], yc[0], yc[1], yc[2], yc[3]};
+#pragma unroll
+  for (int q = 0; q < kQ; ++q)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[q] = fmaf(e4[e], yv[K::idx(q, e)], s[q]);
+}
+
+// Sums of the block's outputs as (max, sum) pairs in log2 units, merged over
+// the waves into sm.cm[0][t], sm.cs[0][t] for output o0 + t.
+template <int KIND>
+__device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
+  using K = BandKind<KIND>;
   const int T = A.T;
-  const int h = blockIdx.z;
-  const int o0 = blockIdx.x * kOut;
   const int lane = lane_id(), w = wave_id();
+  const int tid = threadIdx.x;
   const float* ah = A.a_cur + (int64_t)h * T;
   const float* rh = A.r_cur + (int64_t)h * T;
   const float* zh = A.logz + (int64_t)h * T;
-  const int o = o0 + lane;
-  const int sgn = KIND == 0 ? -1 : 1;
-  const int yoff = KIND == 0 ? kOut - 1 : 0;
-  // summation range: kind 0 rows [o0, T); kind 1 keys [0, T - o0)
+  const int ol = o0 + kQ * lane;  // this lane's first output
+  // summation range: kind 0 rows [o0, T); kind 1 keys [0, T - o0); kind 2
+  // keys [0, min(o0 + kOut, T))
   const int cbeg = KIND == 0 ? o0 : 0;
-  const int cend = KIND == 0 ? T : T - o0;
-  float M = kNegInf, S = 0.f;
-  for (int c0 = cbeg; c0 < cend; c0 += kTK) {
-    float lmx = kNegInf, lmy = kNegInf;
-    for (int x = threadIdx.x; x < kTK; x += kNT) {
-      const int n = c0 + x;
-      float v = kNegInf;
-      if (n < T) v = KIND == 0 ? -zh[n] * kLog2e : ah[n] * kLog2e;
-      sm.x2[x] = v;
-      lmx = fmaxf(lmx, v);
-    }
-    for (int y = threadIdx.x; y < kBand; y += kNT) {
-      float v = kNegInf;
-      if (KIND == 0) {
-        const int d = c0 - o0 - (kOut - 1) + y;
-        if (d >= 0 && d < T) v = rh[d] * kLog2e;
-      } else {
-        const int i = c0 + o0 + y;
-        if (i < T) v = -zh[i] * kLog2e;
-      }
-      sm.y2[y] = v;
-      lmy = fmaxf(lmy, v);
-    }
-    float mx = lmx, my = lmy;
-    block_max2(mx, my, sm.red);
-    if (mx == kNegInf) mx = 0.f;
-    if (my == kNegInf) my = 0.f;
-    for (int x = threadIdx.x; x < kTK; x += kNT) sm.xe[x] = fast_exp2(sm.x2[x] - mx);
-    for (int y = threadIdx.x; y < kBand + 3; y += kNT) {
-      const float e = y < kBand ? fast_exp2(sm.y2[y] - my) : 0.f;
+  const int cend = KIND == 0 ? T : (KIND == 1 ? T - o0 : min(o0 + kOut, T));
+  float M[kQ], S[kQ];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int yy = y - c;
-        if (yy >= 0 && yy < kBS) sm.ye[c * kBS + yy] = e;
+  for (int q = 0; q < kQ; ++q) {
+    M[q] = kNegInf;
+    S[q] = 0.f;
+  }
+  // thread tid stages X entry tid (tid < kTK) and Y entries tid + j kNT
+  constexpr int kYPer = (kBandPad + kNT - 1) / kNT;
+  static_assert(kTK <= kNT, "one X entry per thread at most");
+  // X reads z (kind 0) or a; Y reads z (kind 1) or r.  Their shifts are
+  // upper bounds from the maxima of 256-entry segments (of a, r and -z):
+  // a chunk's X is one segment, its band of kBand entries two.
+  const float* xsrc = KIND == 0 ? zh : ah;
+  const float* ysrc = KIND == 1 ? zh : rh;
+  const int nseg = A.nseg;
+  const float* xmax = (KIND == 0 ? A.smax_z : A.smax_a_cur) + (int64_t)h * nseg;
+  const float* ymax = (KIND == 1 ? A.smax_z : A.smax_r_cur) + (int64_t)h * nseg;
+  constexpr bool XNEG = KIND == 0, YNEG = KIND == 1;
+  // band start (source index of y = 0) of the chunk at c0
+  auto band_lo = [&](int c0) {
+    return KIND == 1 ? c0 + o0 : (KIND == 0 ? c0 - o0 - (kOut - 1) : o0 - c0 - (kTK - 1));
+  };
+  // raw staging values and segment maxima for the chunk at c, loaded a chunk
+  // ahead from clamped (always valid) indices
+  bool okx, oky[kYPer], okm0, okm1;
+  float px, py[kYPer], pmx, pmy0, pmy1;
+  auto prefetch = [&](int c) {
+    px = xsrc[band_x_idx<KIND>(c + tid, T, okx)];
+#pragma unroll
+    for (int j = 0; j < kYPer; ++j) py[j] = ysrc[band_y_idx<KIND>(c, o0, tid + j * kNT, T, oky[j])];
+    // the maxima are the same for every thread; their indices are moved to
+    // vector registers so that the loads are vector loads, which the chunk's
+    // barrier does not wait for (it waits for scalar loads)
+    int ix = min(c / kSegMax, nseg - 1);
+    const int lo = band_lo(c);
+    const int s0 = (lo < 0 ? lo - (kSegMax - 1) : lo) / kSegMax;  // floor
+    okm0 = s0 >= 0 && s0 < nseg;
+    okm1 = s0 + 1 >= 0 && s0 + 1 < nseg;
+    int iy0 = min(max(s0, 0), nseg - 1), iy1 = min(max(s0 + 1, 0), nseg - 1);
+    asm volatile("" : "+v"(ix), "+v"(iy0), "+v"(iy1));
+    pmx = xmax[ix];
+    pmy0 = ymax[iy0];
+    pmy1 = ymax[iy1];
+  };
+  prefetch(cbeg);
+  int par = 0;
+  for (int c0 = cbeg; c0 < cend; c0 += kTK, par ^= 1) {
+    StageBuf& sb = sm.buf[par];
+    const float vx = band_val(px, okx, XNEG);
+    float vy[kYPer];
+#pragma unroll
+    for (int j = 0; j < kYPer; ++j) vy[j] = band_val(py[j], oky[j], YNEG);
+    float mx = pmx * kLog2e;
+    float my = fmaxf(okm0 ? pmy0 * kLog2e : kNegInf, okm1 ? pmy1 * kLog2e : kNegInf);
+    if (!(mx > kNegInf)) mx = 0.f;
+    if (!(my > kNegInf)) my = 0.f;
+    prefetch(c0 + kTK);  // past the range on the last chunk: clamped, unused
+    if (tid < kTK) {
+      sb.x2[tid] = vx;
+      sb.xe[tid] = fast_exp2(vx - mx);
+    }
+#pragma unroll
+    for (int j = 0; j < kYPer; ++j) {
+      const int y = tid + j * kNT;
+      if (y < kBandPad) {
+        sb.y2[y] = vy[j];
+        sb.ye[y] = fast_exp2(vy[j] - my);
       }
     }
+    // one barrier per chunk: it publishes this buffer, and every wave has
+    // finished the chunk before the last, which used the other buffer
     __syncthreads();
 
-    // wave w takes the groups of four x = 4 (w + 4u); x past the summation
-    // range has a zero factor on one side, so all lanes run the same loop
+    // x past the summation range has a zero factor on one side, so every
+    // lane runs the same loop
     const int xlast = min(kTK, cend - c0) - 1;
     const int xq = 4 * __builtin_amdgcn_readfirstlane(w);
-    if (xq <= xlast && o < T) {
-      const int yb = sgn * lane + yoff;  // band index of x = 0
-      const int cpy = yb & 3;            // x is a multiple of 4
-      const lds_f32* yc = (const lds_f32*)sm.ye + cpy * kBS - cpy;
-      const lds_f32* xe = (const lds_f32*)sm.xe;
-      float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-#pragma unroll 4
-      for (int x = xq; x <= xlast; x += 4 * kWaves) {
-        const f32x4 e4 = lds_read_f4(xe + x);
-        const f32x4 y4 = lds_read_f4(yc + (x + yb));
-        s0 = fmaf(e4[0], y4[0], s0);
-        s1 = fmaf(e4[1], y4[1], s1);
-        s2 = fmaf(e4[2], y4[2], s2);
-        s3 = fmaf(e4[3], y4[3], s3);
-      }
-      const float s = (s0 + s1) + (s2 + s3);
-      if (s >= 0x1p-20f) {
-        lse_merge(M, S, mx + my, s);
+    const int ybl = K::SO * kQ * lane + K::OFFB;  // yb - SX x
+    if (xq <= xlast && ol < T) {
+      const lds_f32* xe = (const lds_f32*)sb.xe;
+      const lds_f32* ye = (const lds_f32*)sb.ye;
+      float s[kQ] = {0.f, 0.f, 0.f, 0.f};
+      constexpr int kGroups = kTK / (4 * kWaves);  // groups of a full chunk per wave
+      if (xlast == kTK - 1) {
+        // full chunk: straight-line code, so reads can be issued ahead
+#pragma unroll
+        for (int u = 0; u < kGroups; ++u) {
+          const int x = xq + 4 * kWaves * u;
+          group_fma<KIND>(xe, ye, x, K::SX * x + ybl, s);
+        }
       } else {
-        // exact max-shifted sum of this lane's terms in this wave's groups
-        float cm = kNegInf;
-        for (int g = xq; g <= xlast; g += 4 * kWaves)
-          for (int x = g; x < g + 4 && x <= xlast; ++x) cm = fmaxf(cm, sm.x2[x] + sm.y2[x + yb]);
-        float cs = 0.f;
-        if (cm != kNegInf)
-          for (int g = xq; g <= xlast; g += 4 * kWaves)
-            for (int x = g; x < g + 4 && x <= xlast; ++x) cs += fast_exp2(sm.x2[x] + sm.y2[x + yb] - cm);
-        lse_merge(M, S, cm, cs);
+#pragma unroll 2
+        for (int x = xq; x <= xlast; x += 4 * kWaves) group_fma<KIND>(xe, ye, x, K::SX * x + ybl, s);
+      }
+#pragma unroll
+      for (int q = 0; q < kQ; ++q) {
+        if (ol + q >= T) continue;
+        // a lane sums at most 64 terms of a chunk, each factor <= 1; a term
+        // lost to underflow is below 2^-126 (of 2^(mx + my)), so all lost
+        // terms stay below 2^-120, which is 2^-24 of any sum >= 2^-96
+        if (s[q] >= 0x1p-96f) {
+          lse_merge(M[q], S[q], mx + my, s[q]);
+        } else if (wave_has_terms<KIND>(ol + q, c0, xq, xlast, T)) {
+          const float2 ex = exact_chunk_sum(sb.x2, sb.y2, K::SX, K::SO * (kQ * lane + q) + K::OFF, xq, xlast);
+          lse_merge(M[q], S[q], ex.x, ex.y);
+        }
       }
     }
-    __syncthreads();  // the chunk buffers are restaged next
   }
-  sm.cm[w][lane] = M;
-  sm.cs[w][lane] = S;
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    sm.cm[w][kQ * lane + q] = M[q];
+    sm.cs[w][kQ * lane + q] = S[q];
+  }
   __syncthreads();
-  if (w != 0 || o >= T) return;
   float Mt = kNegInf, St = 0.f;
-  for (int x = 0; x < kWaves; ++x) lse_merge(Mt, St, sm.cm[x][lane], sm.cs[x][lane]);
-  const float theta = KIND == 0 ? ah[o] : rh[o];
-  const float mu = St > 0.f ? St * fast_exp2(theta * kLog2e + Mt) : 0.f;
-  const float eta = (KIND == 0 ? A.eta_abs : A.eta_rel)[(int64_t)h * T + o];
-  const float g = (mu - eta) / (float)T;  // Equation 20
-  const int64_t idx = (int64_t)h * T + o;
-  float* mom1 = KIND == 0 ? A.m_a : A.m_r;
-  float* mom2 = KIND == 0 ? A.v_a : A.v_r;
-  const float m = A.beta1 * mom1[idx] + (1.f - A.beta1) * g;
-  const float v = A.beta2 * mom2[idx] + (1.f - A.beta2) * g * g;
-  mom1[idx] = m;
-  mom2[idx] = v;
-  // theta - lr m_hat / (sqrt(v_hat) + eps) with the bias corrections of step t
-  const float denom = sqrtf(v) * A.inv_sqrt_bc2 + A.eps;
-  (KIND == 0 ? A.a_next : A.r_next)[idx] = theta - A.lr_bc1 * m / denom;
+  if (tid < kOut)
+    for (int x = 0; x < kWaves; ++x) lse_merge(Mt, St, sm.cm[x][tid], sm.cs[x][tid]);
+  __syncthreads();
+  if (tid < kOut) {
+    sm.cm[0][tid] = Mt;
+    sm.cs[0][tid] = St;
+  }
+}
+
+// Gradient and Adam update of parameters o0 .. o0+255 of kind KIND (0: a,
+// 1: r) from the block's marginal sums.
+template <int KIND>
+__device__ void fit_update(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
+  band_sums<KIND>(A, sm, h, o0);
+  const int T = A.T;
+  const int t = threadIdx.x;
+  const int o = o0 + t;
+  float next = kNegInf;
+  if (t < kOut && o < T) {
+    const int64_t idx = (int64_t)h * T + o;
+    const float Mt = sm.cm[0][t], St = sm.cs[0][t];
+    const float theta = (KIND == 0 ? A.a_cur : A.r_cur)[idx];
+    const float mu = St > 0.f ? St * fast_exp2(theta * kLog2e + Mt) : 0.f;
+    const float eta = (KIND == 0 ? A.eta_abs : A.eta_rel)[idx];
+    const float g = (mu - eta) / (float)T;  // Equation 20
+    float* mom1 = KIND == 0 ? A.m_a : A.m_r;
+    float* mom2 = KIND == 0 ? A.v_a : A.v_r;
+    const float m = A.beta1 * mom1[idx] + (1.f - A.beta1) * g;
+    const float v = A.beta2 * mom2[idx] + (1.f - A.beta2) * g * g;
+    mom1[idx] = m;
+    mom2[idx] = v;
+    // theta - lr m_hat / (sqrt(v_hat) + eps) with the bias corrections of step t
+    const float denom = sqrtf(v) * A.inv_sqrt_bc2 + A.eps;
+    next = theta - A.lr_bc1 * m / denom;
+    (KIND == 0 ? A.a_next : A.r_next)[idx] = next;
+  }
+  // the new parameters' maximum over this 256-entry segment
+  const float mx = block_max1(next, sm.red);
+  if (t == 0) (KIND == 0 ? A.smax_a_next : A.smax_r_next)[(int64_t)h * A.nseg + o0 / kSegMax] = mx;
 }
 
 __global__ __launch_bounds__(kNT) void fit_step_kernel(FitStepArgs A) {
   __shared__ StepSmem sm;
+  const int h = blockIdx.z, o0 = blockIdx.x * kOut;
   if (blockIdx.y == 0)
-    fit_step_block<0>(A, sm);
+    fit_update<0>(A, sm, h, o0);
   else
-    fit_step_block<1>(A, sm);
+    fit_update<1>(A, sm, h, o0);
+}
+
+// log N(i) (natural log) of the current parameters into logz, and the
+// maximum of -log N over each 256-row segment into A.smax_z.
+__global__ __launch_bounds__(kNT) void fit_norm_kernel(FitStepArgs A, float* logz) {
+  __shared__ StepSmem sm;
+  const int h = blockIdx.y, o0 = blockIdx.x * kOut;
+  band_sums<2>(A, sm, h, o0);
+  const int o = o0 + (int)threadIdx.x;
+  float nz = kNegInf;
+  if ((int)threadIdx.x < kOut && o < A.T) {
+    const float z = (sm.cm[0][threadIdx.x] + fast_log2(sm.cs[0][threadIdx.x])) * kLn2;
+    logz[(int64_t)h * A.T + o] = z;
+    nz = -z;
+  }
+  const float mx = block_max1(nz, sm.red);
+  if (threadIdx.x == 0) A.smax_z[(int64_t)h * A.nseg + o0 / kSegMax] = mx;
 }
 
 // a = 0, r(d) = log max(eta_rel(d) / (T - d), floor), zero Adam moments.
-__global__ __launch_bounds__(256) void fit_init_kernel(FitStepArgs A) {
+__global__ __launch_bounds__(kSegMax) void fit_init_kernel(FitStepArgs A) {
+  __shared__ float red[8];
   const int h = blockIdx.y;
-  const int d = blockIdx.x * blockDim.x + threadIdx.x;
+  const int d = blockIdx.x * kSegMax + threadIdx.x;
   const int T = A.T;
-  if (d >= T) return;
-  const int64_t idx = (int64_t)h * T + d;
-  A.a_next[idx] = 0.f;
-  A.r_next[idx] = logf(fmaxf(A.eta_rel[idx] / (float)(T - d), kFitInitFloor));
-  A.m_a[idx] = 0.f;
-  A.v_a[idx] = 0.f;
-  A.m_r[idx] = 0.f;
-  A.v_r[idx] = 0.f;
+  float rv = kNegInf;
+  if (d < T) {
+    const int64_t idx = (int64_t)h * T + d;
+    rv = logf(fmaxf(A.eta_rel[idx] / (float)(T - d), kFitInitFloor));
+    A.a_next[idx] = 0.f;
+    A.r_next[idx] = rv;
+    A.m_a[idx] = 0.f;
+    A.v_a[idx] = 0.f;
+    A.m_r[idx] = 0.f;
+    A.v_r[idx] = 0.f;
+  }
+  const float mx = block_max1(rv, red);
+  if (threadIdx.x == 0) {
+    A.smax_a_next[(int64_t)h * A.nseg + blockIdx.x] = 0.f;
+    A.smax_r_next[(int64_t)h * A.nseg + blockIdx.x] = mx;
+  }
 }
 
 // Equation 4 at the final parameters, and kappa = negent / T + loss.
@@ -388,7 +572,7 @@ hipError_t launch_fit_targets(const FitTargetArgs& args, hipStream_t stream) {
 }
 
 hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL(fit_init_kernel, dim3((args.T + 255) / 256, args.n_heads), dim3(256), 0, stream,
+  hipLaunchKernelGGL(fit_init_kernel, dim3(args.nseg, args.n_heads), dim3(kSegMax), 0, stream,
                      args);
   return hipGetLastError();
 }
@@ -396,6 +580,12 @@ hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream) {
 hipError_t launch_fit_step(const FitStepArgs& args, hipStream_t stream) {
   hipLaunchKernelGGL(fit_step_kernel, dim3((args.T + kOut - 1) / kOut, 2, args.n_heads), dim3(kNT), 0,
                      stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t stream) {
+  hipLaunchKernelGGL(fit_norm_kernel, dim3((args.T + kOut - 1) / kOut, args.n_heads), dim3(kNT), 0, stream,
+                     args, logz);
   return hipGetLastError();
 }
 

@@ -162,18 +162,28 @@ struct FitStepArgs {
   float* v_a;
   float* m_r;
   float* v_r;
-  int n_heads, T;
+  // maxima over 256-entry segments ([n][nseg]) of a_cur, r_cur, of the
+  // updated a_next, r_next, and of -logz
+  const float* smax_a_cur;
+  const float* smax_r_cur;
+  float* smax_a_next;
+  float* smax_r_next;
+  float* smax_z;
+  int n_heads, T, nseg;
   float beta1, beta2, eps;
   float lr_bc1;          // lr / (1 - beta1^t)
   float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
 };
 
 constexpr int kFitSegRows = 512;       // rows per partial of the target marginals
+constexpr int kSegMax = 256;           // entries per segment maximum of the fit
 constexpr float kFitInitFloor = 1e-9f;  // floor inside the initial r
 
 hipError_t launch_fit_targets(const FitTargetArgs& args, hipStream_t stream);
 hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream);
 hipError_t launch_fit_step(const FitStepArgs& args, hipStream_t stream);
+// log N of (a_cur, r_cur) into logz (natural log)
+hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t stream);
 hipError_t launch_fit_loss(const FitStepArgs& args, const float* negent, float* loss, float* kappa,
                            hipStream_t stream);
 

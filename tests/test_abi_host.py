@@ -326,9 +326,12 @@ def test_fit_workspace_sizes(b):
     # row sums and entropies [n][T], partial marginals [n][2][ceil(T/512)][T]
     assert L.saf_fit_targets_workspace_bytes(3, 1000) == 2 * _ru(3000 * 4) + _ru(3000 * 2 * 2 * 4)
     assert L.saf_fit_targets_workspace_bytes(36, 4096) == 2 * _ru(36 * 4096 * 4) + _ru(36 * 4096 * 2 * 8 * 4)
-    # second parameter buffer and four moment vectors, 256-byte aligned each
-    assert L.saf_fit_pattern_workspace_bytes(3, 1000) == 6 * _ru(3000 * 4)
-    assert L.saf_fit_pattern_workspace_bytes(1, 1) == 6 * 256
+    # second parameter buffer and four moment vectors, then five arrays of
+    # 256-entry segment maxima (a and r of both buffers, -log N), each
+    # 256-byte aligned
+    assert L.saf_fit_pattern_workspace_bytes(3, 1000) == 6 * _ru(3000 * 4) + 5 * _ru(3 * 4 * 4)
+    assert L.saf_fit_pattern_workspace_bytes(36, 4096) == 6 * _ru(36 * 4096 * 4) + 5 * _ru(36 * 16 * 4)
+    assert L.saf_fit_pattern_workspace_bytes(1, 1) == 11 * 256
     assert L.saf_fit_pattern_workspace_bytes(0, 5) == 0
     assert L.saf_fit_pattern_workspace_bytes(2, (1 << 20) + 1) == 0
 
