@@ -5,7 +5,9 @@ computes, written from "When Can Attention Heads Be Statically Defined?"
 (Section 3, Section 3.2 Equation 3, Appendix A.1 Equations 5-7, Appendix D.2,
 and the trainable-pattern gradients of Appendix C.3.2), and of fitting a
 compact pattern to a calibration mean (``saf_fit_oracle``: Algorithm 1,
-Section 3.2 "Fitting" Equation 4, Appendix A.2, Appendix D.1 Equation 20).
+Section 3.2 "Fitting" Equation 4, Appendix A.2, Appendix D.1 Equation 20),
+and of the calibration statistics (``saf_calib_oracle``: Section 3.1,
+Equations 1 and 2).
 It exists only to check the HIP library.  Only ``tests/``,
 ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
 import it; the library and its Python binding never do, and nothing here
@@ -15,7 +17,7 @@ Every function is pinned by a CPU test to something other than itself
 (closed forms, a hand-worked example, library routines, finite differences).
 """
 
-from . import saf_fit_oracle
+from . import saf_calib_oracle, saf_fit_oracle
 from .saf_oracle import (
     frozen_head_bwd,
     frozen_head_fwd,
@@ -35,6 +37,7 @@ from .saf_oracle import (
 )
 
 __all__ = [
+    "saf_calib_oracle",
     "saf_fit_oracle",
     "frozen_head_bwd",
     "frozen_head_fwd",
