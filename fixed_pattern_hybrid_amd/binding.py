@@ -37,6 +37,8 @@ EXPORTED = (
     "saf_fit_targets_workspace_bytes",
     "saf_fit_pattern",
     "saf_fit_pattern_workspace_bytes",
+    "saf_calib_stats",
+    "saf_calib_stats_workspace_bytes",
     "saf_status_string",
     "saf_version",
 )
@@ -111,6 +113,11 @@ def _load():
     lib.saf_fit_pattern.restype = ctypes.c_int
     lib.saf_fit_pattern_workspace_bytes.argtypes = [i32, i32]
     lib.saf_fit_pattern_workspace_bytes.restype = sz
+    lib.saf_calib_stats.argtypes = [i32, i32, i32, i32, f32, vp, ctypes.POINTER(ctypes.c_int64), vp,
+                                    ctypes.POINTER(ctypes.c_int64), vp, i64, i64, vp, vp, vp, sz, vp]
+    lib.saf_calib_stats.restype = ctypes.c_int
+    lib.saf_calib_stats_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.saf_calib_stats_workspace_bytes.restype = sz
     lib.saf_status_string.argtypes = [ctypes.c_int]
     lib.saf_status_string.restype = ctypes.c_char_p
     lib.saf_version.argtypes = []
@@ -461,3 +468,42 @@ def saf_fit_pattern(eta_abs: torch.Tensor, eta_rel: torch.Tensor, negent: Option
                                _ptr(out["logz"]), _ptr(out["loss"]), _ptr(out["kappa"]), _ptr(ws),
                                ws.numel(), _stream_handle(stream)), "saf_fit_pattern")
     return out
+
+
+# ---------------------------------------------------------------------------
+# Calibration statistics.
+# ---------------------------------------------------------------------------
+
+
+def calib_stats_workspace_bytes(N: int, H: int, T: int) -> int:
+    return int(LIB.saf_calib_stats_workspace_bytes(int(N), int(H), int(T)))
+
+
+def saf_calib_stats(q: torch.Tensor, k: torch.Tensor, softmax_scale: Optional[float] = None,
+                    ahat: Optional[torch.Tensor] = None, workspace=None, stream=None):
+    """Mean attention and the two scores of H heads over N calibration
+    sequences: q, k bf16 [N, H, T, D] on one GPU.  Returns (ahat [H, T, T]
+    fp32, s_var [H] fp64, s_kl [H] fp64); a freshly allocated ahat is zero
+    above the diagonal (the library writes only causal entries)."""
+    for name, t in (("q", q), ("k", k)):
+        if t.dtype != torch.bfloat16 or t.dim() != 4 or not t.is_cuda or t.stride(3) != 1:
+            raise ValueError(f"{name} must be a bfloat16 [N, H, T, D] GPU tensor with contiguous D")
+    if q.shape != k.shape or q.device != k.device:
+        raise ValueError("q and k must have the same shape and device")
+    N, H, T, D = q.shape
+    dev = q.device
+    if ahat is None:
+        ahat = torch.zeros((H, T, T), dtype=torch.float32, device=dev)
+    if ahat.dtype != torch.float32 or ahat.dim() != 3 or tuple(ahat.shape[:2]) != (H, T) or ahat.shape[2] < T \
+            or ahat.stride(2) != 1 or ahat.device != dev:
+        raise ValueError("ahat must be float32 [H, T, >= T] with a contiguous last dimension")
+    s_var = torch.empty((H,), dtype=torch.float64, device=dev)
+    s_kl = torch.empty((H,), dtype=torch.float64, device=dev)
+    ws = _workspace(calib_stats_workspace_bytes(N, H, T), dev, workspace)
+    qs = (ctypes.c_int64 * 3)(q.stride(0), q.stride(1), q.stride(2))
+    ks = (ctypes.c_int64 * 3)(k.stride(0), k.stride(1), k.stride(2))
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(LIB.saf_calib_stats(N, H, T, D, scale, _ptr(q), qs, _ptr(k), ks, _ptr(ahat), ahat.stride(0),
+                               ahat.stride(1), _ptr(s_var), _ptr(s_kl), _ptr(ws), ws.numel(),
+                               _stream_handle(stream)), "saf_calib_stats")
+    return ahat, s_var, s_kl

@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "kern_pattern.hip", "kern_fwd.hip", "kern_bwd.hip", "kern_f32.hip", "kern_pgrad.hip", "kern_fit.hip"]
+SOURCES = ["abi.hip", "kern_pattern.hip", "kern_fwd.hip", "kern_bwd.hip", "kern_f32.hip", "kern_pgrad.hip", "kern_fit.hip", "kern_calib.hip"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",

@@ -554,4 +554,67 @@ int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const floa
   return SAF_OK;
 }
 
+namespace {
+
+bool calib_sizes_ok(int32_t N, int32_t H, int32_t T) {
+  return N >= 1 && N <= 65535 && H >= 1 && H <= 65535 && T >= 1 && T <= SAF_MAX_T;
+}
+
+size_t calib_ws(int32_t N, int32_t H, int32_t T) {
+  const size_t nqb = ((size_t)T + saf::kCalibBM - 1) / saf::kCalibBM;
+  const size_t nprog = nqb * (nqb + 1);
+  return round_up((size_t)N * H * T * sizeof(float), 256) + round_up((size_t)H * nprog * 3 * sizeof(double), 256);
+}
+
+bool calib_tensor_ok(const void* p, const int64_t* st, int32_t D) {
+  if (!p || !st || !aligned(p, 16)) return false;
+  for (int x = 0; x < 3; ++x)
+    if (st[x] < 0 || st[x] % 8 != 0) return false;
+  return st[2] >= D && st[2] <= SAF_MAX_T_STRIDE;
+}
+
+}  // namespace
+
+size_t saf_calib_stats_workspace_bytes(int32_t N, int32_t H, int32_t T) {
+  return calib_sizes_ok(N, H, T) ? calib_ws(N, H, T) : 0;
+}
+
+int saf_calib_stats(int32_t N, int32_t H, int32_t T, int32_t D, float softmax_scale, const void* q,
+                    const int64_t q_stride[3], const void* k, const int64_t k_stride[3], float* ahat,
+                    int64_t ahat_head_stride, int64_t ahat_row_stride, double* s_var, double* s_kl,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!calib_sizes_ok(N, H, T)) return SAF_EINVAL;
+  if (D != 64 && D != 96 && D != 128) return SAF_EUNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return SAF_EINVAL;
+  if (!calib_tensor_ok(q, q_stride, D) || !calib_tensor_ok(k, k_stride, D)) return SAF_EINVAL;
+  if (!ahat || !aligned(ahat, 4) || ahat_row_stride < T || ahat_head_stride < 0) return SAF_EINVAL;
+  if (!s_var || !s_kl || !aligned(s_var, 8) || !aligned(s_kl, 8)) return SAF_EINVAL;
+  const size_t need = calib_ws(N, H, T);
+  if (!ws || !aligned(ws, 256) || ws_bytes < need) return SAF_EWORKSPACE;
+  const int nqb = (T + saf::kCalibBM - 1) / saf::kCalibBM;
+  const int64_t nprog = (int64_t)nqb * (nqb + 1);
+  if (nprog > INT32_MAX) return SAF_EUNSUPPORTED;
+  saf::CalibArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.q = TensorRef{const_cast<void*>(q), q_stride[0], q_stride[1], q_stride[2]};
+  ca.k = TensorRef{const_cast<void*>(k), k_stride[0], k_stride[1], k_stride[2]};
+  ca.ahat = ahat;
+  ca.ld_a = ahat_row_stride;
+  ca.head_a = ahat_head_stride;
+  char* w = static_cast<char*>(ws);
+  ca.lse2 = reinterpret_cast<float*>(w);
+  ca.part = reinterpret_cast<double*>(w + round_up((size_t)N * H * T * sizeof(float), 256));
+  ca.s_var = s_var;
+  ca.s_kl = s_kl;
+  ca.N = N;
+  ca.H = H;
+  ca.T = T;
+  ca.nqb = nqb;
+  ca.nprog = (int)nprog;
+  ca.ahat_vec = aligned(ahat, 16) && ahat_row_stride % 4 == 0 && ahat_head_stride % 4 == 0;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.f / std::sqrt((float)D);
+  ca.scale_log2 = scale * 1.4426950408889634f;
+  return saf::launch_calib(ca, D, stream) == hipSuccess ? SAF_OK : SAF_EHIP;
+}
+
 }  // extern "C"

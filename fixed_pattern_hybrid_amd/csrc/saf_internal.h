@@ -187,6 +187,26 @@ hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t str
 hipError_t launch_fit_loss(const FitStepArgs& args, const float* negent, float* loss, float* kappa,
                            hipStream_t stream);
 
+// Calibration statistics over N sequences of ordinary heads.
+struct CalibArgs {
+  TensorRef q, k;     // bf16 [N][H][T][D]: sb is the sequence stride
+  float* ahat;        // [H] heads head_a apart, rows ld_a floats apart
+  int64_t ld_a, head_a;
+  float* lse2;        // workspace [N][H][T]: row log-sum-exp (log2 units)
+  double* part;       // workspace [H][nprog][3]: per-program sums
+  double* s_var;      // [H]
+  double* s_kl;       // [H]
+  int N, H, T;
+  int nqb, nprog;     // query blocks; programs per head nqb (nqb + 1)
+  int ahat_vec;       // every row of ahat starts 16-byte aligned
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+constexpr int kCalibBM = 128;  // queries per calibration program
+constexpr int kCalibBN = 64;   // keys per calibration tile
+
+hipError_t launch_calib(const CalibArgs& args, int D, hipStream_t stream);
+
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program
 constexpr int kBwdKvBN = 128;   // keys per key-block program

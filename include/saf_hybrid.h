@@ -300,6 +300,46 @@ int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const floa
 /* Workspace bytes saf_fit_pattern needs (0 for invalid sizes). */
 size_t saf_fit_pattern_workspace_bytes(int32_t n_heads, int32_t T);
 
+/*
+ * Calibration statistics of attention heads ("When Can Attention Heads Be
+ * Statically Defined?", Section 3.1, Equations 1 and 2; Algorithm 1 measures
+ * them before fitting).  For each of H heads, over N calibration sequences,
+ * with A^(n) the causal row softmax of s * Q^(n) K^(n)T (Appendix A.1,
+ * Equations 5-6; s = softmax_scale, or 1/sqrt(D) when softmax_scale <= 0):
+ *   ahat[h][i][j] = N^-1 sum_n A^(n)[i][j]                      for j <= i
+ *   s_var[h] = sum_n sum_{i,j} (A^(n)[i][j] - ahat[i][j])^2 / ((N - 1) T^2)
+ *              (0 when N = 1)
+ *   s_kl[h]  = (N T)^-1 sum_n sum_i KL(A^(n)[i][0..i] || ahat[i][0..i])
+ * in one pass over the sequences without storing any A^(n): the running
+ * mean and squared deviations of every entry (Welford's update) are kept
+ * on chip, and the KL sum uses sum_n KL = sum_n sum A ln A - N sum
+ * ahat ln ahat.  Entries above the diagonal of ahat are not written.
+ *   q, k        : device bf16 [N][H][T][D] with element strides
+ *                 (sequence, head, row) in q_stride / k_stride; last
+ *                 dimension contiguous; 16-byte aligned, strides multiples
+ *                 of 8 elements, row stride at most SAF_MAX_T_STRIDE.
+ *   ahat        : device fp32 output; row i of head h at
+ *                 ahat + h * ahat_head_stride + i * ahat_row_stride;
+ *                 4-byte aligned, row stride >= T, head stride >= 0 (rows
+ *                 that all start 16-byte aligned are written 16 bytes at a
+ *                 time).
+ *   s_var, s_kl : device fp64 [H] outputs.
+ *   ws          : saf_calib_stats_workspace_bytes(N, H, T) bytes, 256-byte
+ *                 aligned: row log-sum-exps and per-program partial sums
+ *                 (reduced in a fixed order: bitwise deterministic).
+ * Scores and probabilities are fp32 (bf16 products on MFMA); partial sums of
+ * the scores are fp64.  D in {64, 96, 128}; N in [1, 65535]; H in
+ * [1, 65535]; T in [1, SAF_MAX_T].
+ */
+int saf_calib_stats(int32_t N, int32_t H, int32_t T, int32_t D, float softmax_scale,
+                    const void* q, const int64_t q_stride[3], const void* k,
+                    const int64_t k_stride[3], float* ahat, int64_t ahat_head_stride,
+                    int64_t ahat_row_stride, double* s_var, double* s_kl, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes saf_calib_stats needs (0 for invalid sizes). */
+size_t saf_calib_stats_workspace_bytes(int32_t N, int32_t H, int32_t T);
+
 /* Static description of a status code (never NULL). */
 const char* saf_status_string(int status);
 

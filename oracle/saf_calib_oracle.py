@@ -29,38 +29,49 @@ import numpy as np
 F64 = np.float64
 
 
-def attention_matrix(q, k, scale: float) -> np.ndarray:
-    """A = causal row softmax of scale * Q K^T (Appendix A.1, Equations
-    5-6) for one head and one sequence: q, k are [T, D]; returns [T, T]
-    with zeros above the diagonal."""
+def attention_rows(q, k, scale: float, rows) -> np.ndarray:
+    """Rows ``rows`` of A = causal row softmax of scale * Q K^T (Appendix
+    A.1, Equations 5-6) for one head and one sequence: q, k are [T, D];
+    returns [len(rows), T] with zeros at keys j > i."""
     q = np.asarray(q, dtype=F64)
     k = np.asarray(k, dtype=F64)
     T = q.shape[0]
-    S = scale * (q @ k.T)
-    causal = np.tril(np.ones((T, T), dtype=bool))
-    S = np.where(causal, S, -np.inf)
+    rows = np.asarray(rows, dtype=np.int64)
+    S = scale * (q[rows] @ k.T)
+    S = np.where(np.arange(T)[None, :] <= rows[:, None], S, -np.inf)
     m = S.max(axis=1, keepdims=True)
     E = np.exp(S - m)
     return E / E.sum(axis=1, keepdims=True)
 
 
+def attention_matrix(q, k, scale: float) -> np.ndarray:
+    """The whole [T, T] causal attention matrix of one head and sequence."""
+    return attention_rows(q, k, scale, np.arange(np.shape(q)[0]))
+
+
+def calibration_rows(q, k, scale: float, rows) -> Dict[str, object]:
+    """The part of one head's statistics that rows ``rows`` determine: the
+    mean rows A-hat[rows] and the rows' terms of the two score sums,
+    ``sq`` = sum_n sum_{i in rows} ||A^(n)[i] - A-hat[i]||^2 and
+    ``kl`` = sum_n sum_{i in rows} KL(A^(n)[i] || A-hat[i]).  Both scores
+    are sums over rows, so the rows of a partition add up to the whole."""
+    q = np.asarray(q, dtype=F64)
+    k = np.asarray(k, dtype=F64)
+    N = q.shape[0]
+    As = np.stack([attention_rows(q[n], k[n], scale, rows) for n in range(N)])
+    Ahat = As.mean(axis=0)
+    sq = float(((As - Ahat[None]) ** 2).sum())
+    kl = 0.0
+    for n in range(N):
+        pos = As[n] > 0
+        kl += float((As[n][pos] * (np.log(As[n][pos]) - np.log(Ahat[pos]))).sum())
+    return {"ahat": Ahat, "sq": sq, "kl": kl}
+
+
 def calibration_stats(q, k, scale: float) -> Dict[str, object]:
     """A-hat, s_var and s_KL of one head from its N calibration sequences:
     q, k are [N, T, D]."""
-    q = np.asarray(q, dtype=F64)
-    k = np.asarray(k, dtype=F64)
-    N, T, _ = q.shape
-    As = np.stack([attention_matrix(q[n], k[n], scale) for n in range(N)])
-    Ahat = As.mean(axis=0)
-    if N > 1:
-        s_var = float(((As - Ahat[None]) ** 2).sum() / ((N - 1) * T * T))
-    else:
-        s_var = 0.0
-    causal = np.tril(np.ones((T, T), dtype=bool))
-    kl = 0.0
-    for n in range(N):
-        P = As[n][causal]
-        Q = Ahat[causal]
-        pos = P > 0
-        kl += float((P[pos] * (np.log(P[pos]) - np.log(Q[pos]))).sum())
-    return {"ahat": Ahat, "s_var": s_var, "s_kl": kl / (N * T)}
+    N, T, _ = np.shape(q)
+    part = calibration_rows(q, k, scale, np.arange(T))
+    s_var = part["sq"] / ((N - 1) * T * T) if N > 1 else 0.0
+    return {"ahat": part["ahat"], "s_var": s_var, "s_kl": part["kl"] / (N * T)}

@@ -400,3 +400,41 @@ def test_fit_binding_checks_without_gpu(b):
         b.saf_fit_targets(torch.zeros(4, 4))  # not a GPU tensor
     with pytest.raises(ValueError):
         b.saf_fit_pattern(torch.zeros(2, 4), torch.zeros(2, 4))
+
+
+def test_calib_workspace_and_rejects(b):
+    L = b.LIB
+    # row log-sum-exps [N][H][T] fp32, then [H][nqb (nqb + 1)][3] fp64 partials
+    nqb = -(-300 // 128)
+    assert L.saf_calib_stats_workspace_bytes(4, 3, 300) == _ru(4 * 3 * 300 * 4) + _ru(3 * nqb * (nqb + 1) * 3 * 8)
+    assert L.saf_calib_stats_workspace_bytes(0, 3, 300) == 0
+    assert L.saf_calib_stats_workspace_bytes(4, 0, 300) == 0
+    assert L.saf_calib_stats_workspace_bytes(4, 3, 0) == 0
+    N, H, T, D = 2, 2, 100, 64
+    need = L.saf_calib_stats_workspace_bytes(N, H, T)
+    st = (ctypes.c_int64 * 3)(H * T * D, T * D, D)
+    ok = dict(N=N, H=H, T=T, D=D, scale=0.0, q=FAKE, qs=st, k=FAKE, ks=st, a=FAKE, ah=T * T, ar=T,
+              sv=FAKE, sk=FAKE, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        x = {**ok, **kw}
+        return L.saf_calib_stats(x["N"], x["H"], x["T"], x["D"], x["scale"], x["q"], x["qs"], x["k"], x["ks"],
+                                 x["a"], x["ah"], x["ar"], x["sv"], x["sk"], x["ws"], x["wsb"], None)
+
+    assert call(N=0) == -1
+    assert call(T=0) == -1
+    assert call(D=80) == -2
+    assert call(scale=float("nan")) == -1
+    assert call(q=None) == -1
+    assert call(k=FAKE + 8) == -1  # 16-byte alignment
+    bad = (ctypes.c_int64 * 3)(H * T * D, T * D, D + 4)  # row stride not a multiple of 8
+    assert call(qs=bad) == -1
+    short = (ctypes.c_int64 * 3)(H * T * D, T * D, 32)  # rows shorter than D
+    assert call(ks=short) == -1
+    assert call(a=FAKE + 2) == -1
+    assert call(ar=T - 1) == -1
+    assert call(ah=-4) == -1
+    assert call(sv=FAKE + 4) == -1  # fp64 alignment
+    assert call(sk=None) == -1
+    assert call(ws=None) == -3
+    assert call(wsb=need - 1) == -3

@@ -114,3 +114,13 @@ def test_invariants():
     k2[:, -1] += 5.0
     st4 = C.calibration_stats(q, k2, 0.25)
     np.testing.assert_allclose(st4["ahat"][:-1], st["ahat"][:-1], rtol=0, atol=0)
+
+
+def test_rows_partition_adds_up():
+    N, T, D = 3, 19, 4
+    q, k = _qk(N, T, D, 8, sigma=1.5)
+    full = C.calibration_stats(q, k, 0.5)
+    parts = [C.calibration_rows(q, k, 0.5, r) for r in (np.arange(0, 7), np.arange(7, 12), np.arange(12, T))]
+    assert sum(p["sq"] for p in parts) / ((N - 1) * T * T) == pytest.approx(full["s_var"], rel=1e-12)
+    assert sum(p["kl"] for p in parts) / (N * T) == pytest.approx(full["s_kl"], rel=1e-12)
+    np.testing.assert_allclose(np.concatenate([p["ahat"] for p in parts]), full["ahat"], rtol=0, atol=0)
