@@ -274,6 +274,67 @@ def pattern_fit_leg(B, stream, reps: int = 5):
     }
 
 
+# Calibration time the pages print for the 124M model at 4K (Table 13,
+# "Capture and mean" column, 25% rate, three-seed mean; GH200): running the
+# model on 32 sequences, capturing every head's attention and averaging it.
+PAGES_CALIB_S_124M = 51.56
+
+
+def calibration_leg(B, stream, reps: int = 3):
+    """Calibration statistics of the 124M model: mean attention, variance and
+    forward-KL scores of its 144 heads (12 layers x 12) over 32 sequences of
+    4096 tokens, from queries and keys resident in HBM.  The synthetic
+    activations of one layer's 12 heads are used for every layer (the work
+    does not depend on the values).  Reported apart from the layer step."""
+    import numpy as np
+    import torch
+
+    from synth.calib import CALIB_WORKLOADS, calibration_qk
+
+    wl = CALIB_WORKLOADS["gpt2_124m_4k"]
+    N, H, T, D = wl.N, wl.H, wl.T, wl.D
+    layers = 12
+    q1, k1 = calibration_qk(N, H, T, D, wl.seed)
+    q = torch.from_numpy(q1).cuda().to(torch.bfloat16).repeat(1, layers, 1, 1)
+    k = torch.from_numpy(k1).cuda().to(torch.bfloat16).repeat(1, layers, 1, 1)
+    del q1, k1
+    Ht = H * layers
+    ahat = torch.zeros((Ht, T, T), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(B.calib_stats_workspace_bytes(N, Ht, T), 256), dtype=torch.uint8, device="cuda")
+
+    def call():
+        return B.saf_calib_stats(q, k, ahat=ahat, workspace=ws, stream=stream)
+
+    _, s_var, s_kl = call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    pairs_ = T * (T + 1) // 2
+    updates = Ht * N * pairs_  # (head, sequence, causal entry) updates of the statistics
+    # per update: the score's log2 probability (1 FMA), its exponential, the
+    # Welford update (2 subtractions, 2 FMAs) and the A log A sum (1 FMA):
+    # 10 fp32 flops counted (the exponential not counted)
+    flops = 10 * updates
+    ach = flops / (ms * 1e-3) / 1e12
+    order = np.argsort(s_var.cpu().numpy()[:H])
+    return {
+        "workload": wl.name, "heads": Ht, "sequences": N, "T": T, "D": D,
+        "ms": round(ms, 3), "updates_per_s": round(updates / (ms * 1e-3), 1),
+        "lowest_variance_heads_of_layer": [int(x) for x in order[:3]],
+        "pages_capture_and_mean_s": PAGES_CALIB_S_124M,
+        "roofline": {"bound": "alu", "achieved": round(ach, 2), "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F32_TFLOPS, 4), "kernel": "calib_lse + calib_stats (whole call)",
+                     "flops_per_call": flops},
+        "note": "pages' figure: GH200, whole-model forward passes with attention capture (Table 13); "
+                "here the statistics from resident queries and keys only; context, not a target",
+    }
+
+
 # Attention-operation prefill speedups the pages print for the Qwen3-4B
 # grouped-query path over all-ordinary attention (Table 26, in parentheses),
 # keyed by (B, T, replaced fraction in percent).
@@ -403,6 +464,9 @@ def main():
     ap.add_argument("--no-fit", action="store_true",
                     help="skip the pattern-fitting leg (36 fits at T=4096, reported apart from value)")
     ap.add_argument("--fit-only", action="store_true", help="run only the pattern-fitting leg")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip the calibration-statistics leg (144 heads, 32 x 4096 tokens, apart from value)")
+    ap.add_argument("--calib-only", action="store_true", help="run only the calibration-statistics leg")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
@@ -423,6 +487,9 @@ def main():
 
     if args.fit_only:
         print(json.dumps({"pattern_fit": pattern_fit_leg(B, torch.cuda.current_stream())}), flush=True)
+        return
+    if args.calib_only:
+        print(json.dumps({"calibration": calibration_leg(B, torch.cuda.current_stream())}), flush=True)
         return
 
     cfg = CONFIGS[args.config]
@@ -540,6 +607,8 @@ def main():
         out["attention_op_speedup"] = fwd_speedup_vs_ordinary(B, cfg, q, k, v, a, r, fz)
     if not args.no_fit and args.config == DEFAULT_CONFIG:
         out["pattern_fit"] = pattern_fit_leg(B, stream)
+    if not args.no_calib and args.config == DEFAULT_CONFIG:
+        out["calibration"] = calibration_leg(B, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_budget)
     print(json.dumps(out), flush=True)

@@ -28,6 +28,8 @@
 // Products are transposed (S^T = K Q^T) so that a lane owns one query: lane
 // l of wave w holds query q0 + 32 w + l % 32 and keys
 // j0 + 32 c + 8 (r / 4) + 4 (l / 32) + r % 4 of its two accumulators.
+#include <type_traits>
+
 #include "saf_internal.h"
 #include "saf_tile.h"
 
@@ -88,36 +90,61 @@ __global__ __launch_bounds__(256) void calib_lse_kernel(CalibArgs A) {
   kdma.issue(kg, A.k.st, 0, T, smem);
   wait_vm_loads();
   __syncthreads();
+  // Online log-sum-exp with a lazy reference maximum (as in the forward):
+  // exponentials are taken against m (log2 units) and the tile maximum is
+  // only formed when a lane's sum exceeds 2^8 (the first tile, a grown
+  // maximum, or a rare false alarm); the result is exact for any reference.
   float m = kNegInf, sum = 0.f;
-  for (int t = 0; t < ntiles; ++t) {
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int j0 = t * kBN;
     const bool more = t + 1 < ntiles;
     if (more) kdma.issue(kg, A.k.st, j0 + kBN, T, smem + ((t + 1) & 1) * C::TILE);
     f32x16 s[2];
     score_tile<D>(smem + (t & 1) * C::TILE, qf, s);
-    float tmax = kNegInf;
+    if constexpr (MASK) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const float x = j <= i ? s[c][r] * sl2 : kNegInf;
-        s[c][r] = x;
-        tmax = fmaxf(tmax, x);
-      }
-    if (tmax > kNegInf) {
-      const float mn = fmaxf(m, tmax);
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
+          if (j > i) s[c][r] = kNegInf;
+        }
+    }
+    auto exps = [&](float ref) {
       float ps = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ps += fast_exp2(s[c][r] - mn);
-      sum = sum * fast_exp2(m - mn) + ps;
-      m = mn;
+        for (int r = 0; r < 16; ++r) ps += fast_exp2(fmaf(s[c][r], sl2, -ref));
+      return ps;
+    };
+    float ps = exps(m);
+    if (__any(!(ps <= 256.f))) {
+      asm volatile("");
+      float mx = kNegInf;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+      const float mn = fmaxf(m, mx * sl2);
+      if (mn > kNegInf) {
+        sum *= fast_exp2(m - mn);
+        m = mn;
+        ps = exps(m);
+      } else {
+        ps = 0.f;  // no key of this tile reaches the lane's query yet
+      }
     }
+    sum += ps;
     if (more) wait_vm_loads();
     __syncthreads();
-  }
+  };
+  // tiles wholly below the block's first query need no mask
+  const int t_diag = min(q0 / kBN, ntiles);
+  int t = 0;
+  for (; t < t_diag; ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
   // merge the two halves of the lane pair that share a query
   const float mo = xor32(m), so = xor32(sum);
   const float mt = fmaxf(m, mo);
@@ -202,7 +229,10 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
   kdma.issue(kbase(0), A.k.st, j0, T, smem);
   wait_vm_loads();
   __syncthreads();
-  for (int n = 0; n < A.N; ++n) {
+  // tiles wholly below the diagonal, in query blocks inside [0, T), need no mask
+  const bool nomask = j0 + kBN - 1 <= q0 && q0 + kBM <= T;
+  auto step = [&](auto mask_tag, int n) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const bool more = n + 1 < A.N;
     float lse_n = 0.f;
     if (more) {
@@ -218,7 +248,7 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool ok = valid(c, r);
+        const bool ok = !MASK || valid(c, r);
         const float xl = fmaf(s[c][r], sl2, -lse);  // log2 A
         const float a = ok ? fast_exp2(xl) : 0.f;
         alog = ok ? fmaf(a, xl, alog) : alog;
@@ -236,7 +266,11 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
       wait_vm_loads();
     }
     __syncthreads();
-  }
+  };
+  if (nomask)
+    for (int n = 0; n < A.N; ++n) step(std::false_type{}, n);
+  else
+    for (int n = 0; n < A.N; ++n) step(std::true_type{}, n);
 
   // store the mean of the causal entries; sums for the scores
   double sm2 = 0.0, shat = 0.0;
