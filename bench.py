@@ -62,6 +62,28 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_kv_gpt2-124m-layer_B8
 KERNEL_SOURCES = ("kern_bwd.hip", "saf_device.h", "saf_tile.h", "saf_internal.h")
 
 
+# Measured v_exp_f32 issue time on gfx950: 3.9 ns per wave instruction per
+# SIMD (64 exponentials), 1024 SIMDs.
+EXP_PER_S = 64 / 3.9e-9 * 1024
+
+
+def exp_counts(cfg, with_bwd: bool):
+    """Exponentials per step as this design computes them (ordinary heads:
+    one per causal pair and (b, h) in the forward and one in each of the
+    backward's two recomputing passes; frozen heads: one per pair, shared by
+    a batch group of two, in the forward and in the backward's dV; the
+    normalisers' T(T+1)/2 per frozen head), and the time they take at the
+    measured exponential rate."""
+    P = pairs(cfg.T)
+    n_frz = len(cfg.frozen)
+    n_ord = cfg.H - n_frz
+    groups = (cfg.B + 1) // 2
+    fwd = P * cfg.B * n_ord + P * groups * n_frz + P * n_frz
+    bwd = (2 * P * cfg.B * n_ord + P * groups * n_frz) if with_bwd else 0
+    n = fwd + bwd
+    return {"count": n, "fwd": fwd, "bwd": bwd, "bound_ms": round(n / EXP_PER_S * 1e3, 4)}
+
+
 def kernel_source_sha() -> str:
     """Hash of the sources the key-block kernel is compiled from."""
     import hashlib
@@ -142,20 +164,34 @@ def per_head_costs(B, cfg, reps: int = 10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    def q(xs, p):
+        return float(np.percentile(np.asarray(xs) / cfg.H, p))
+
     out = {}
     for with_bwd, tag in ((False, "fwd"), (True, "fwd_bwd")):
         run(res["ordinary"], with_bwd)
         run(res["frozen"], with_bwd)
         samples = {"ordinary": [], "frozen": []}
-        for order in (("ordinary", "frozen"), ("frozen", "ordinary")) * 2:
+        for order in (("ordinary", "frozen"), ("frozen", "ordinary")) * 4:
             for kind in order:
                 samples[kind].append(run(res[kind], with_bwd))
-        o_ms = float(np.median(samples["ordinary"])) / cfg.H
-        f_ms = float(np.median(samples["frozen"])) / cfg.H
+        o_ms, f_ms = q(samples["ordinary"], 50), q(samples["frozen"], 50)
+        o_iqr = [round(q(samples["ordinary"], 25), 5), round(q(samples["ordinary"], 75), 5)]
+        f_iqr = [round(q(samples["frozen"], 25), 5), round(q(samples["frozen"], 75), 5)]
         out[tag] = {"ordinary_ms_per_head": round(o_ms, 5), "frozen_ms_per_head": round(f_ms, 5),
-                    "frozen_over_ordinary": round(f_ms / o_ms, 3)}
+                    "frozen_over_ordinary": round(f_ms / o_ms, 3),
+                    "ordinary_iqr": o_iqr, "frozen_iqr": f_iqr,
+                    # frozen median below the ordinary one with disjoint interquartile ranges
+                    "frozen_cheaper": bool(f_ms < o_ms and f_iqr[1] < o_iqr[0])}
+    # zero-replacement control: the same all-ordinary call against itself in
+    # A-B-B-A order; the comparison above is trusted only if this stays ~1.00
+    ctl = {"a": [], "b": []}
+    for order in (("a", "b"), ("b", "a")) * 4:
+        for x in order:
+            ctl[x].append(run(res["ordinary"], True))
+    out["zero_replacement_control"] = round(float(np.median(ctl["b"]) / np.median(ctl["a"])), 4)
     out["note"] = (f"same shape (B={cfg.B}, T={cfg.T}, d={cfg.D}), all {cfg.H} heads ordinary vs all frozen; "
-                   "median of 4 A/B/B/A-ordered samples of 10 calls each")
+                   "median and quartiles of 8 A/B/B/A-ordered samples of 10 calls each")
     return out
 
 
@@ -435,10 +471,19 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
     dt = time.perf_counter() - t0
     f = flops(cfg, n_ord=done_ord, n_frz=done_frz, B=1)
     fl = f["total"] if inp.do is not None else f["fwd"]
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {
         "value": fl / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "cpu_model": model,
         "kind": "oracle",
         "sample": f"float64 dense oracle, fwd+bwd of {done_ord} ordinary + {done_frz} frozen whole "
                   f"(batch, head) slices (T={cfg.T}, d={cfg.D}) in {dt:.1f} s; "
@@ -557,6 +602,9 @@ def main():
             for x, n in enumerate(names_b):
                 per[n].append(bevs[s][x].elapsed_time(bevs[s][x + 1]))
     kern_ms = {n: float(np.mean(v_)) for n, v_ in per.items() if v_}
+    # per-step durations: from the first forward event to the last one of the
+    # step (the backward's when it runs)
+    step_ms = [fevs[s][0].elapsed_time(bevs[s][-1] if do is not None else fevs[s][-1]) for s in range(K)]
 
     f = flops(cfg)
     total = f["total"] if do is not None else f["fwd"]
@@ -594,6 +642,12 @@ def main():
         "mfma_util": round(value / PEAK_BF16_TFLOPS, 4),
         "tokens_per_s": round(tokens, 1),
         "kernel_ms": {n: round(x, 4) for n, x in kern_ms.items()},
+        "fwd_ms": round(sum(kern_ms[n] for n in names_f), 4),
+        "bwd_ms": round(sum(kern_ms[n] for n in names_b), 4) if do is not None else None,
+        "step_ms_median": round(float(np.median(step_ms)), 4),
+        "step_ms_min": round(float(np.min(step_ms)), 4),
+        "step_ms_p90": round(float(np.percentile(step_ms, 90)), 4),
+        "exp": exp_counts(cfg, do is not None),
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
