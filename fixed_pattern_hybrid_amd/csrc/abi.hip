@@ -430,10 +430,16 @@ size_t fit_targets_ws(int32_t n_heads, int32_t T) {
   return 2 * round_up(nT * sizeof(float), 256) + round_up(nT * 2 * nseg * sizeof(float), 256);
 }
 
+size_t fit_maxg(int32_t T) {
+  const size_t nseg = ((size_t)T + saf::kSegMax - 1) / saf::kSegMax;
+  return (nseg + saf::kFitGroupChunks - 1) / saf::kFitGroupChunks;
+}
+
 size_t fit_pattern_ws(int32_t n_heads, int32_t T) {
   const size_t nseg = ((size_t)T + saf::kSegMax - 1) / saf::kSegMax;
+  const size_t part = (size_t)n_heads * fit_maxg(T) * (size_t)T * 2 * sizeof(float);
   return 6 * round_up((size_t)n_heads * (size_t)T * sizeof(float), 256) +
-         5 * round_up((size_t)n_heads * nseg * sizeof(float), 256);
+         5 * round_up((size_t)n_heads * nseg * sizeof(float), 256) + round_up(part, 256) + round_up(2 * part, 256);
 }
 
 }  // namespace
@@ -511,6 +517,10 @@ int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const floa
   float* sa[2] = {reinterpret_cast<float*>(w + 6 * vec), reinterpret_cast<float*>(w + 6 * vec + segv)};
   float* sr[2] = {reinterpret_cast<float*>(w + 6 * vec + 2 * segv), reinterpret_cast<float*>(w + 6 * vec + 3 * segv)};
   fa.smax_z = reinterpret_cast<float*>(w + 6 * vec + 4 * segv);
+  const size_t part = (size_t)n_heads * fit_maxg(T) * (size_t)T * 2 * sizeof(float);
+  fa.part_z = reinterpret_cast<float2*>(w + 6 * vec + 5 * segv);
+  fa.part_m = reinterpret_cast<float2*>(w + 6 * vec + 5 * segv + round_up(part, 256));
+  fa.maxg = (int)fit_maxg(T);
   fa.n_heads = n_heads;
   fa.T = T;
   fa.nseg = (T + saf::kSegMax - 1) / saf::kSegMax;

@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void fit_negent_kernel(FitTargetArgs A) {
 // ---------------------------------------------------------------------------
 
 constexpr int kQ = 4;                 // parameters per lane
+constexpr int kGrp = kFitGroupChunks;  // chunks per block at most
 #ifndef SAF_FIT_WAVES
 #define SAF_FIT_WAVES 4
 #endif
@@ -314,10 +315,28 @@ __device__ __forceinline__ void group_fma(const lds_f32* xe, const lds_f32* ye, 
     for (int e = 0; e < 4; ++e) s[q] = fmaf(e4[e], yv[K::idx(q, e)], s[q]);
 }
 
-// Sums of the block's outputs as (max, sum) pairs in log2 units, merged over
-// the waves into sm.cm[0][t], sm.cs[0][t] for output o0 + t.
+// Summation range of an output block (chunks of kTK from cbeg to cend):
+// kind 0 rows [o0, T); kind 1 keys [0, T - o0); kind 2 keys [0, min(o0 +
+// kOut, T)).  A block sums one group of at most kGrp chunks.
 template <int KIND>
-__device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
+__device__ __forceinline__ void sum_range(int o0, int T, int& cbeg, int& cend) {
+  cbeg = KIND == 0 ? o0 : 0;
+  cend = KIND == 0 ? T : (KIND == 1 ? T - o0 : min(o0 + kOut, T));
+}
+
+template <int KIND>
+__device__ __forceinline__ int n_groups(int o0, int T) {
+  int cbeg, cend;
+  sum_range<KIND>(o0, T, cbeg, cend);
+  const int chunks = (cend - cbeg + kTK - 1) / kTK;
+  return (chunks + kGrp - 1) / kGrp;
+}
+
+// Sums of the block's outputs over chunk group grp, as (max, sum) pairs in
+// log2 units, merged over the waves into sm.cm[0][t], sm.cs[0][t] for output
+// o0 + t.
+template <int KIND>
+__device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0, int grp) {
   using K = BandKind<KIND>;
   const int T = A.T;
   const int lane = lane_id(), w = wave_id();
@@ -326,10 +345,10 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
   const float* rh = A.r_cur + (int64_t)h * T;
   const float* zh = A.logz + (int64_t)h * T;
   const int ol = o0 + kQ * lane;  // this lane's first output
-  // summation range: kind 0 rows [o0, T); kind 1 keys [0, T - o0); kind 2
-  // keys [0, min(o0 + kOut, T))
-  const int cbeg = KIND == 0 ? o0 : 0;
-  const int cend = KIND == 0 ? T : (KIND == 1 ? T - o0 : min(o0 + kOut, T));
+  int cbeg, cend;
+  sum_range<KIND>(o0, T, cbeg, cend);
+  cbeg += grp * kGrp * kTK;
+  cend = min(cend, cbeg + kGrp * kTK);
   float M[kQ], S[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -455,20 +474,75 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
   }
 }
 
-// Gradient and Adam update of parameters o0 .. o0+255 of kind KIND (0: a,
-// 1: r) from the block's marginal sums.
+// Partial sums of one chunk group of an output block: (max, sum) per output
+// into part[(slot * maxg + grp) * T + o].
 template <int KIND>
-__device__ void fit_update(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
-  band_sums<KIND>(A, sm, h, o0);
+__device__ void band_part(const FitStepArgs& A, StepSmem& sm, int h, int o0, int grp, float2* part,
+                          int64_t slot) {
+  if (grp >= n_groups<KIND>(o0, A.T)) return;  // whole block
+  band_sums<KIND>(A, sm, h, o0, grp);
+  const int t = threadIdx.x;
+  if (t < kOut && o0 + t < A.T)
+    part[(slot * A.maxg + grp) * A.T + o0 + t] = make_float2(sm.cm[0][t], sm.cs[0][t]);
+}
+
+// (max, sum) of output o over its groups, merged in group order.
+__device__ __forceinline__ float2 merge_groups(const float2* part, int64_t slot, int maxg, int T, int o, int ng) {
+  float M = kNegInf, S = 0.f;
+  for (int g = 0; g < ng; ++g) {
+    const float2 p = part[(slot * maxg + g) * T + o];
+    lse_merge(M, S, p.x, p.y);
+  }
+  return make_float2(M, S);
+}
+
+// Grid (output blocks, chunk groups, heads): partial normaliser sums.
+__global__ __launch_bounds__(kNT) void fit_norm_part_kernel(FitStepArgs A) {
+  __shared__ StepSmem sm;
+  band_part<2>(A, sm, blockIdx.z, blockIdx.x * kOut, blockIdx.y, A.part_z, blockIdx.z);
+}
+
+// Grid (output blocks, chunk groups, 2 x heads): partial marginal sums.
+__global__ __launch_bounds__(kNT) void fit_marg_part_kernel(FitStepArgs A) {
+  __shared__ StepSmem sm;
+  const int h = blockIdx.z >> 1;
+  if (blockIdx.z & 1)
+    band_part<1>(A, sm, h, blockIdx.x * kOut, blockIdx.y, A.part_m, blockIdx.z);
+  else
+    band_part<0>(A, sm, h, blockIdx.x * kOut, blockIdx.y, A.part_m, blockIdx.z);
+}
+
+// Grid (output blocks, heads): log N(i) (natural log) of the current
+// parameters into logz from the groups' partials, and the maximum of -log N
+// over each 256-row segment into A.smax_z.
+__global__ __launch_bounds__(kSegMax) void fit_norm_merge_kernel(FitStepArgs A, float* logz) {
+  __shared__ float red[kSegMax / 64];
+  const int h = blockIdx.y, o0 = blockIdx.x * kOut;
+  const int o = o0 + (int)threadIdx.x;
+  float nz = kNegInf;
+  if (o < A.T) {
+    const float2 p = merge_groups(A.part_z, h, A.maxg, A.T, o, n_groups<2>(o0, A.T));
+    const float z = (p.x + fast_log2(p.y)) * kLn2;
+    logz[(int64_t)h * A.T + o] = z;
+    nz = -z;
+  }
+  const float mx = block_max1(nz, red);
+  if (threadIdx.x == 0) A.smax_z[(int64_t)h * A.nseg + o0 / kSegMax] = mx;
+}
+
+// Gradient and Adam update of parameters o0 .. o0+255 of kind KIND (0: a,
+// 1: r) from the groups' marginal partials.
+template <int KIND>
+__device__ void fit_update(const FitStepArgs& A, float* red, int h, int o0) {
   const int T = A.T;
   const int t = threadIdx.x;
   const int o = o0 + t;
   float next = kNegInf;
-  if (t < kOut && o < T) {
+  if (o < T) {
     const int64_t idx = (int64_t)h * T + o;
-    const float Mt = sm.cm[0][t], St = sm.cs[0][t];
+    const float2 p = merge_groups(A.part_m, 2 * h + KIND, A.maxg, T, o, n_groups<KIND>(o0, T));
     const float theta = (KIND == 0 ? A.a_cur : A.r_cur)[idx];
-    const float mu = St > 0.f ? St * fast_exp2(theta * kLog2e + Mt) : 0.f;
+    const float mu = p.y > 0.f ? p.y * fast_exp2(theta * kLog2e + p.x) : 0.f;
     const float eta = (KIND == 0 ? A.eta_abs : A.eta_rel)[idx];
     const float g = (mu - eta) / (float)T;  // Equation 20
     float* mom1 = KIND == 0 ? A.m_a : A.m_r;
@@ -483,34 +557,18 @@ __device__ void fit_update(const FitStepArgs& A, StepSmem& sm, int h, int o0) {
     (KIND == 0 ? A.a_next : A.r_next)[idx] = next;
   }
   // the new parameters' maximum over this 256-entry segment
-  const float mx = block_max1(next, sm.red);
+  const float mx = block_max1(next, red);
   if (t == 0) (KIND == 0 ? A.smax_a_next : A.smax_r_next)[(int64_t)h * A.nseg + o0 / kSegMax] = mx;
 }
 
-__global__ __launch_bounds__(kNT) void fit_step_kernel(FitStepArgs A) {
-  __shared__ StepSmem sm;
+// Grid (output blocks, 2, heads).
+__global__ __launch_bounds__(kSegMax) void fit_update_kernel(FitStepArgs A) {
+  __shared__ float red[kSegMax / 64];
   const int h = blockIdx.z, o0 = blockIdx.x * kOut;
   if (blockIdx.y == 0)
-    fit_update<0>(A, sm, h, o0);
+    fit_update<0>(A, red, h, o0);
   else
-    fit_update<1>(A, sm, h, o0);
-}
-
-// log N(i) (natural log) of the current parameters into logz, and the
-// maximum of -log N over each 256-row segment into A.smax_z.
-__global__ __launch_bounds__(kNT) void fit_norm_kernel(FitStepArgs A, float* logz) {
-  __shared__ StepSmem sm;
-  const int h = blockIdx.y, o0 = blockIdx.x * kOut;
-  band_sums<2>(A, sm, h, o0);
-  const int o = o0 + (int)threadIdx.x;
-  float nz = kNegInf;
-  if ((int)threadIdx.x < kOut && o < A.T) {
-    const float z = (sm.cm[0][threadIdx.x] + fast_log2(sm.cs[0][threadIdx.x])) * kLn2;
-    logz[(int64_t)h * A.T + o] = z;
-    nz = -z;
-  }
-  const float mx = block_max1(nz, sm.red);
-  if (threadIdx.x == 0) A.smax_z[(int64_t)h * A.nseg + o0 / kSegMax] = mx;
+    fit_update<1>(A, red, h, o0);
 }
 
 // a = 0, r(d) = log max(eta_rel(d) / (T - d), floor), zero Adam moments.
@@ -578,14 +636,16 @@ hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream) {
 }
 
 hipError_t launch_fit_step(const FitStepArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL(fit_step_kernel, dim3((args.T + kOut - 1) / kOut, 2, args.n_heads), dim3(kNT), 0,
-                     stream, args);
+  const int nb = (args.T + kOut - 1) / kOut;
+  hipLaunchKernelGGL(fit_marg_part_kernel, dim3(nb, args.maxg, 2 * args.n_heads), dim3(kNT), 0, stream, args);
+  hipLaunchKernelGGL(fit_update_kernel, dim3(nb, 2, args.n_heads), dim3(kSegMax), 0, stream, args);
   return hipGetLastError();
 }
 
 hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t stream) {
-  hipLaunchKernelGGL(fit_norm_kernel, dim3((args.T + kOut - 1) / kOut, args.n_heads), dim3(kNT), 0, stream,
-                     args, logz);
+  const int nb = (args.T + kOut - 1) / kOut;
+  hipLaunchKernelGGL(fit_norm_part_kernel, dim3(nb, args.maxg, args.n_heads), dim3(kNT), 0, stream, args);
+  hipLaunchKernelGGL(fit_norm_merge_kernel, dim3(nb, args.n_heads), dim3(kSegMax), 0, stream, args, logz);
   return hipGetLastError();
 }
 

@@ -169,7 +169,11 @@ struct FitStepArgs {
   float* smax_a_next;
   float* smax_r_next;
   float* smax_z;
-  int n_heads, T, nseg;
+  // (max, sum) partials of chunk groups: normalisers [n][maxg][T],
+  // marginals [n][2][maxg][T]
+  float2* part_z;
+  float2* part_m;
+  int n_heads, T, nseg, maxg;
   float beta1, beta2, eps;
   float lr_bc1;          // lr / (1 - beta1^t)
   float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
@@ -177,6 +181,7 @@ struct FitStepArgs {
 
 constexpr int kFitSegRows = 512;       // rows per partial of the target marginals
 constexpr int kSegMax = 256;           // entries per segment maximum of the fit
+constexpr int kFitGroupChunks = 4;     // chunks of 256 summation indices per fit block
 constexpr float kFitInitFloor = 1e-9f;  // floor inside the initial r
 
 hipError_t launch_fit_targets(const FitTargetArgs& args, hipStream_t stream);

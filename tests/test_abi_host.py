@@ -326,12 +326,19 @@ def test_fit_workspace_sizes(b):
     # row sums and entropies [n][T], partial marginals [n][2][ceil(T/512)][T]
     assert L.saf_fit_targets_workspace_bytes(3, 1000) == 2 * _ru(3000 * 4) + _ru(3000 * 2 * 2 * 4)
     assert L.saf_fit_targets_workspace_bytes(36, 4096) == 2 * _ru(36 * 4096 * 4) + _ru(36 * 4096 * 2 * 8 * 4)
-    # second parameter buffer and four moment vectors, then five arrays of
-    # 256-entry segment maxima (a and r of both buffers, -log N), each
-    # 256-byte aligned
-    assert L.saf_fit_pattern_workspace_bytes(3, 1000) == 6 * _ru(3000 * 4) + 5 * _ru(3 * 4 * 4)
-    assert L.saf_fit_pattern_workspace_bytes(36, 4096) == 6 * _ru(36 * 4096 * 4) + 5 * _ru(36 * 16 * 4)
-    assert L.saf_fit_pattern_workspace_bytes(1, 1) == 11 * 256
+    # second parameter buffer and four moment vectors, five arrays of
+    # 256-entry segment maxima (a and r of both buffers, -log N), then float2
+    # partials of chunk groups (4 chunks of 256) for the normalisers and both
+    # marginals, each 256-byte aligned
+    def fit_ws(n, T):
+        nseg = -(-T // 256)
+        maxg = -(-nseg // 4)
+        part = n * maxg * T * 8
+        return 6 * _ru(n * T * 4) + 5 * _ru(n * nseg * 4) + _ru(part) + _ru(2 * part)
+    assert L.saf_fit_pattern_workspace_bytes(3, 1000) == fit_ws(3, 1000)
+    assert L.saf_fit_pattern_workspace_bytes(36, 4096) == fit_ws(36, 4096)
+    assert fit_ws(36, 4096) == 6 * _ru(36 * 4096 * 4) + 5 * _ru(36 * 16 * 4) + 3 * 36 * 4 * 4096 * 8
+    assert L.saf_fit_pattern_workspace_bytes(1, 1) == 13 * 256
     assert L.saf_fit_pattern_workspace_bytes(0, 5) == 0
     assert L.saf_fit_pattern_workspace_bytes(2, (1 << 20) + 1) == 0
 
