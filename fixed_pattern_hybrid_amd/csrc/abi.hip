@@ -96,11 +96,17 @@ size_t bwd_ws_bytes(const saf_attn_params* p) {
 }
 
 // bf16 forward with frozen heads: normaliser partials, one float2 per
-// (frozen head, key group, row), at most 32 groups.  The fp32 forward needs
+// (frozen head, key group, row), at most 32 groups, then the maxima of the
+// frozen heads' a and r over 256-entry segments.  The fp32 forward needs
 // none.
+size_t lz_part_bytes(const saf_attn_params* p, int n_frz) {
+  return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
+}
+
 size_t fwd_ws_bytes(const saf_attn_params* p, int n_frz) {
   if (p->dtype != SAF_BF16 || n_frz == 0 || p->logz) return 0;
-  return round_up((size_t)n_frz * saf::lognorm_groups(p->T) * p->T * 2 * sizeof(float), 256);
+  const size_t nseg = ((size_t)p->T + saf::kSegMax - 1) / saf::kSegMax;
+  return lz_part_bytes(p, n_frz) + round_up(2 * (size_t)n_frz * nseg * sizeof(float), 256);
 }
 
 // Pattern gradients: D_b of frozen rows; for bf16 also, per program (frozen
@@ -236,7 +242,24 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
       args.lz_part = static_cast<const float2*>(ws);
       args.lz_group = saf::lognorm_group_keys(p->T);
       args.lz_ngroups = saf::lognorm_groups(p->T);
-      if (saf::launch_lognorm_partial(la, static_cast<float2*>(ws), args.lz_group, stream) != hipSuccess)
+      // the band-sum program of the fit, over the frozen heads' rows of a, r
+      saf::FitStepArgs na;
+      std::memset(&na, 0, sizeof(na));
+      na.a_cur = a;
+      na.r_cur = r;
+      na.prm_stride = p->prior_len;
+      na.use_heads = 1;
+      std::memcpy(na.heads, args.frz_heads, sizeof(na.heads));
+      na.n_heads = n_frz;
+      na.T = p->T;
+      na.nseg = (p->T + saf::kSegMax - 1) / saf::kSegMax;
+      na.grp_chunks = args.lz_group / saf::kSegMax;
+      na.maxg = args.lz_ngroups;
+      na.part_z = static_cast<float2*>(ws);
+      float* smax = reinterpret_cast<float*>(static_cast<char*>(ws) + lz_part_bytes(p, n_frz));
+      na.smax_a_cur = smax;
+      na.smax_r_cur = smax + (size_t)n_frz * na.nseg;
+      if (saf::launch_lognorm_band(na, smax, smax + (size_t)n_frz * na.nseg, stream) != hipSuccess)
         return SAF_EHIP;
     } else {
       if (saf::launch_lognorm(la, stream) != hipSuccess) return SAF_EHIP;
@@ -521,6 +544,9 @@ int saf_fit_pattern(int32_t n_heads, int32_t T, const float* eta_abs, const floa
   fa.part_z = reinterpret_cast<float2*>(w + 6 * vec + 5 * segv);
   fa.part_m = reinterpret_cast<float2*>(w + 6 * vec + 5 * segv + round_up(part, 256));
   fa.maxg = (int)fit_maxg(T);
+  fa.grp_chunks = saf::kFitGroupChunks;
+  fa.prm_stride = T;
+  fa.use_heads = 0;
   fa.n_heads = n_heads;
   fa.T = T;
   fa.nseg = (T + saf::kSegMax - 1) / saf::kSegMax;

@@ -169,7 +169,6 @@ __global__ __launch_bounds__(256) void fit_negent_kernel(FitTargetArgs A) {
 // ---------------------------------------------------------------------------
 
 constexpr int kQ = 4;                 // parameters per lane
-constexpr int kGrp = kFitGroupChunks;  // chunks per block at most
 #ifndef SAF_FIT_WAVES
 #define SAF_FIT_WAVES 4
 #endif
@@ -317,7 +316,7 @@ __device__ __forceinline__ void group_fma(const lds_f32* xe, const lds_f32* ye, 
 
 // Summation range of an output block (chunks of kTK from cbeg to cend):
 // kind 0 rows [o0, T); kind 1 keys [0, T - o0); kind 2 keys [0, min(o0 +
-// kOut, T)).  A block sums one group of at most kGrp chunks.
+// kOut, T)).  A block sums one group of at most A.grp_chunks chunks.
 template <int KIND>
 __device__ __forceinline__ void sum_range(int o0, int T, int& cbeg, int& cend) {
   cbeg = KIND == 0 ? o0 : 0;
@@ -325,11 +324,11 @@ __device__ __forceinline__ void sum_range(int o0, int T, int& cbeg, int& cend) {
 }
 
 template <int KIND>
-__device__ __forceinline__ int n_groups(int o0, int T) {
+__device__ __forceinline__ int n_groups(int o0, int T, int gchunks) {
   int cbeg, cend;
   sum_range<KIND>(o0, T, cbeg, cend);
   const int chunks = (cend - cbeg + kTK - 1) / kTK;
-  return (chunks + kGrp - 1) / kGrp;
+  return (chunks + gchunks - 1) / gchunks;
 }
 
 // Sums of the block's outputs over chunk group grp, as (max, sum) pairs in
@@ -341,14 +340,15 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0, int
   const int T = A.T;
   const int lane = lane_id(), w = wave_id();
   const int tid = threadIdx.x;
-  const float* ah = A.a_cur + (int64_t)h * T;
-  const float* rh = A.r_cur + (int64_t)h * T;
+  const int hp = A.use_heads ? (int)A.heads[h] : h;  // row of a and r
+  const float* ah = A.a_cur + (int64_t)hp * A.prm_stride;
+  const float* rh = A.r_cur + (int64_t)hp * A.prm_stride;
   const float* zh = A.logz + (int64_t)h * T;
   const int ol = o0 + kQ * lane;  // this lane's first output
   int cbeg, cend;
   sum_range<KIND>(o0, T, cbeg, cend);
-  cbeg += grp * kGrp * kTK;
-  cend = min(cend, cbeg + kGrp * kTK);
+  cbeg += grp * A.grp_chunks * kTK;
+  cend = min(cend, cbeg + A.grp_chunks * kTK);
   float M[kQ], S[kQ];
 #pragma unroll
   for (int q = 0; q < kQ; ++q) {
@@ -479,7 +479,7 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0, int
 template <int KIND>
 __device__ void band_part(const FitStepArgs& A, StepSmem& sm, int h, int o0, int grp, float2* part,
                           int64_t slot) {
-  if (grp >= n_groups<KIND>(o0, A.T)) return;  // whole block
+  if (grp >= n_groups<KIND>(o0, A.T, A.grp_chunks)) return;  // whole block
   band_sums<KIND>(A, sm, h, o0, grp);
   const int t = threadIdx.x;
   if (t < kOut && o0 + t < A.T)
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kSegMax) void fit_norm_merge_kernel(FitStepArgs A, 
   const int o = o0 + (int)threadIdx.x;
   float nz = kNegInf;
   if (o < A.T) {
-    const float2 p = merge_groups(A.part_z, h, A.maxg, A.T, o, n_groups<2>(o0, A.T));
+    const float2 p = merge_groups(A.part_z, h, A.maxg, A.T, o, n_groups<2>(o0, A.T, A.grp_chunks));
     const float z = (p.x + fast_log2(p.y)) * kLn2;
     logz[(int64_t)h * A.T + o] = z;
     nz = -z;
@@ -540,7 +540,7 @@ __device__ void fit_update(const FitStepArgs& A, float* red, int h, int o0) {
   float next = kNegInf;
   if (o < T) {
     const int64_t idx = (int64_t)h * T + o;
-    const float2 p = merge_groups(A.part_m, 2 * h + KIND, A.maxg, T, o, n_groups<KIND>(o0, T));
+    const float2 p = merge_groups(A.part_m, 2 * h + KIND, A.maxg, T, o, n_groups<KIND>(o0, T, A.grp_chunks));
     const float theta = (KIND == 0 ? A.a_cur : A.r_cur)[idx];
     const float mu = p.y > 0.f ? p.y * fast_exp2(theta * kLog2e + p.x) : 0.f;
     const float eta = (KIND == 0 ? A.eta_abs : A.eta_rel)[idx];
@@ -569,6 +569,25 @@ __global__ __launch_bounds__(kSegMax) void fit_update_kernel(FitStepArgs A) {
     fit_update<0>(A, red, h, o0);
   else
     fit_update<1>(A, red, h, o0);
+}
+
+// Grid (segments, listed heads): maxima of a and r over each 256-entry
+// segment [0, T) of the listed heads' rows.
+__global__ __launch_bounds__(kSegMax) void norm_segmax_kernel(FitStepArgs A, float* smax_a, float* smax_r) {
+  __shared__ float red[kSegMax / 64];
+  const int h = blockIdx.y;
+  const int hp = A.use_heads ? (int)A.heads[h] : h;
+  const int x = blockIdx.x * kSegMax + threadIdx.x;
+  const bool ok = x < A.T;
+  const float va = ok ? A.a_cur[(int64_t)hp * A.prm_stride + x] : kNegInf;
+  const float vr = ok ? A.r_cur[(int64_t)hp * A.prm_stride + x] : kNegInf;
+  const float ma = block_max1(va, red);
+  __syncthreads();  // red is reused
+  const float mr = block_max1(vr, red);
+  if (threadIdx.x == 0) {
+    smax_a[(int64_t)h * A.nseg + blockIdx.x] = ma;
+    smax_r[(int64_t)h * A.nseg + blockIdx.x] = mr;
+  }
 }
 
 // a = 0, r(d) = log max(eta_rel(d) / (T - d), floor), zero Adam moments.
@@ -646,6 +665,15 @@ hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t str
   const int nb = (args.T + kOut - 1) / kOut;
   hipLaunchKernelGGL(fit_norm_part_kernel, dim3(nb, args.maxg, args.n_heads), dim3(kNT), 0, stream, args);
   hipLaunchKernelGGL(fit_norm_merge_kernel, dim3(nb, args.n_heads), dim3(kSegMax), 0, stream, args, logz);
+  return hipGetLastError();
+}
+
+hipError_t launch_lognorm_band(const FitStepArgs& args, float* smax_a, float* smax_r, hipStream_t stream) {
+  if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(norm_segmax_kernel, dim3(args.nseg, args.n_heads), dim3(kSegMax), 0, stream, args, smax_a,
+                     smax_r);
+  const int nb = (args.T + kOut - 1) / kOut;
+  hipLaunchKernelGGL(fit_norm_part_kernel, dim3(nb, args.maxg, args.n_heads), dim3(kNT), 0, stream, args);
   return hipGetLastError();
 }
 

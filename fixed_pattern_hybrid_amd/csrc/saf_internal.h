@@ -174,9 +174,13 @@ struct FitStepArgs {
   float2* part_z;
   float2* part_m;
   int n_heads, T, nseg, maxg;
+  int grp_chunks;       // chunks of 256 summation indices per block group
+  int64_t prm_stride;   // elements between the a (and r) rows of two heads
+  int use_heads;        // a, r row of listed head x is heads[x] (else x)
   float beta1, beta2, eps;
   float lr_bc1;          // lr / (1 - beta1^t)
   float inv_sqrt_bc2;    // 1 / sqrt(1 - beta2^t)
+  uint8_t heads[kMaxHeads];
 };
 
 constexpr int kFitSegRows = 512;       // rows per partial of the target marginals
@@ -189,6 +193,11 @@ hipError_t launch_fit_init(const FitStepArgs& args, hipStream_t stream);
 hipError_t launch_fit_step(const FitStepArgs& args, hipStream_t stream);
 // log N of (a_cur, r_cur) into logz (natural log)
 hipError_t launch_fit_norm(const FitStepArgs& args, float* logz, hipStream_t stream);
+// Normaliser partials of the listed heads for the forward: segment maxima of
+// their a and r rows into smax_a / smax_r ([n][nseg]), then (max, sum)
+// partials over key groups of grp_chunks * 256 keys into part_z
+// ([n][maxg][T], log2 units).
+hipError_t launch_lognorm_band(const FitStepArgs& args, float* smax_a, float* smax_r, hipStream_t stream);
 hipError_t launch_fit_loss(const FitStepArgs& args, const float* negent, float* loss, float* kappa,
                            hipStream_t stream);
 

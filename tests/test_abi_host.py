@@ -154,13 +154,18 @@ def test_grid_size_limits(b):
 
 
 def test_fwd_workspace_checks(b):
+    # normaliser partials (float2 per frozen head, key group, row), then the
+    # maxima of the frozen heads' a and r over 256-entry segments
+    def fwd_ws(n_frz, groups, T):
+        return _ru(n_frz * groups * T * 8) + _ru(2 * n_frz * -(-T // 256) * 4)
+
     T = 2100  # nine key groups of 256
     p, arr = _params(b, B=2, H=4, T=T, frozen=[0, 1, 0, 1])
     need = b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0)
-    assert need == -(-(2 * 9 * T * 8) // 256) * 256
+    assert need == fwd_ws(2, 9, T)
     for T2, groups in ((256, 1), (257, 2), (8192, 32), (8193, 17), (32768, 32), (1 << 20, 32)):
         p2, arr2 = _params(b, B=1, H=4, T=T2, frozen=[0, 1, 0, 1])
-        assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p2), 0) == -(-(2 * groups * T2 * 8) // 256) * 256
+        assert b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p2), 0) == fwd_ws(2, groups, T2)
     args = [FAKE] * 7
     assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, None, need, None) == -3
     assert b.LIB.saf_hybrid_attn_fwd(ctypes.byref(p), *args, FAKE, need - 1, None) == -3
