@@ -15,12 +15,10 @@
 // (max, sum) pairs in log2 units merged as a log-sum-exp.
 //
 //   lognorm_kernel          one block per (head, row block), all chunks in
-//                           turn; writes log N (natural log).
-//   lognorm_partial_kernel  one block per (head, row block, key group of one
-//                           or more chunks); writes the group's (max, sum)
-//                           pair per row, merged later by the forward's
-//                           frozen programs.  This spreads the triangular
-//                           work over many more blocks.
+//                           turn; writes log N (natural log).  Used by
+//                           saf_pattern_lognorm and the fp32 forward; the
+//                           bf16 forward takes key-group partials from the
+//                           band-sum program of kern_fit.hip.
 #include "saf_internal.h"
 #include "saf_device.h"
 #include "saf_tile.h"
@@ -192,33 +190,6 @@ __global__ __launch_bounds__(kNT) void lognorm_kernel(LognormArgs A, int identit
   }
 }
 
-// Grid: (row blocks, key groups, listed heads); group g covers keys
-// [g * group_keys, (g + 1) * group_keys), processed kTK keys at a time.
-// Writes float2 (max, sum) at part[(hidx * ngroups + g) * T + i] for the rows
-// i >= the group's first key.
-__global__ __launch_bounds__(kNT) void lognorm_partial_kernel(LognormArgs A, float2* part, int group_keys) {
-  __shared__ ChunkSmem sm;
-  const int hidx = blockIdx.z;
-  const int h = A.heads[hidx];
-  const int T = A.T;
-  const int i0 = blockIdx.x * kRows;
-  const int kb = blockIdx.y * group_keys;
-  const int last_row = min(i0 + kRows, T) - 1;
-  if (kb > last_row) return;  // no row of this block reaches the group (whole block)
-  const int kend = min(kb + group_keys, last_row + 1);
-  const float* arow = A.a + (int64_t)h * A.prior_len;
-  const float* rrow = A.r + (int64_t)h * A.prior_len;
-  float M = kNegInf, S = 0.f;
-  for (int k0 = kb; k0 < kend; k0 += kTK) {
-    float cm, cs;
-    chunk_partial(arow, rrow, T, i0, k0, sm, cm, cs);
-    lse_merge(M, S, cm, cs);
-  }
-  const int i = i0 + lane_id();
-  if (wave_id() == 0 && i < T && kb <= i)
-    part[((int64_t)hidx * gridDim.y + blockIdx.y) * T + i] = make_float2(M, S);
-}
-
 // Dense eager pattern of one head: row i per block, exact max-shifted sum.
 __device__ __forceinline__ float block_max(float v, float* red) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -266,15 +237,6 @@ hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream) 
   if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
   dim3 grid((args.T + kRows - 1) / kRows, args.n_heads);
   hipLaunchKernelGGL(lognorm_kernel, grid, dim3(kNT), 0, stream, args, 1);
-  return hipGetLastError();
-}
-
-hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, int group_keys,
-                                  hipStream_t stream) {
-  if (args.n_heads <= 0 || args.T <= 0) return hipSuccess;
-  if (group_keys <= 0 || group_keys % kTK != 0) return hipErrorInvalidValue;
-  dim3 grid((args.T + kRows - 1) / kRows, (args.T + group_keys - 1) / group_keys, args.n_heads);
-  hipLaunchKernelGGL(lognorm_partial_kernel, grid, dim3(kNT), 0, stream, args, part, group_keys);
   return hipGetLastError();
 }
 

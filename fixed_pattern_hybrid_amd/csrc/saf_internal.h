@@ -106,7 +106,6 @@ struct LognormArgs {
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_lognorm(const LognormArgs& args, hipStream_t stream);
-hipError_t launch_lognorm_partial(const LognormArgs& args, float2* part, int group_keys, hipStream_t stream);
 hipError_t launch_pattern_dense(int T, int prior_len, const float* a, const float* r, float* w,
                                 hipStream_t stream);
 
