@@ -14,10 +14,14 @@
 //   calib_stats_kernel  program (query block, key tile, head): for each
 //                       sequence in turn the 128 x 64 score tile is
 //                       recomputed on MFMA, A = exp2(s - lse), and every
-//                       entry's running mean and sum of squared deviations
-//                       are updated in registers (Welford's update), so the
-//                       variance needs no second pass; sum A log A is
-//                       accumulated on the way.  Since log A-hat does not
+//                       entry's sums of deviations from its first
+//                       sequence's value, s1 = sum (A - A0) and s2 =
+//                       sum (A - A0)^2, are accumulated in registers (the
+//                       shifted-data algorithm of Chan, Golub and LeVeque:
+//                       mean = A0 + s1/N, sum of squared deviations =
+//                       s2 - s1^2/N, stable because A0 is one of the
+//                       samples), so the variance needs no second pass;
+//                       sum A log A is accumulated on the way.  Since log A-hat does not
 //                       depend on n, sum_n KL(A^(n) || A-hat) =
 //                       sum_n sum A log A - N sum A-hat log A-hat, which the
 //                       program completes from its final mean.  The tile's
@@ -205,11 +209,14 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
   const int i = q0 + 32 * w + (l & 31);
   const float sl2 = A.scale_log2;
 
-  f32x16 mean[2], m2[2];
+  // shifted sums (shift = the first sequence's value): s1 = sum (a - a0),
+  // s2 = sum (a - a0)^2
+  f32x16 a0[2], s1[2], s2[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    mean[c] = f32x16{};
-    m2[c] = f32x16{};
+    a0[c] = f32x16{};
+    s1[c] = f32x16{};
+    s2[c] = f32x16{};
   }
   double alogA = 0.0;  // sum over sequences of this lane's A log2 A
   // causal entries of this lane: key j <= i (and i < T)
@@ -231,8 +238,9 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
   __syncthreads();
   // tiles wholly below the diagonal, in query blocks inside [0, T), need no mask
   const bool nomask = j0 + kBN - 1 <= q0 && q0 + kBM <= T;
-  auto step = [&](auto mask_tag, int n) {
+  auto step = [&](auto mask_tag, auto first_tag, int n) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     const bool more = n + 1 < A.N;
     float lse_n = 0.f;
     if (more) {
@@ -242,7 +250,6 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
     }
     f32x16 s[2];
     score_tile<D>(smem + (n & 1) * C::TILE, qf, s);
-    const float inv_n = 1.f / (float)(n + 1);
     float alog = 0.f;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -252,11 +259,13 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
         const float xl = fmaf(s[c][r], sl2, -lse);  // log2 A
         const float a = ok ? fast_exp2(xl) : 0.f;
         alog = ok ? fmaf(a, xl, alog) : alog;
-        // Welford: mean_n = mean_{n-1} + (a - mean_{n-1}) / n,
-        // M2_n = M2_{n-1} + (a - mean_{n-1}) (a - mean_n)
-        const float d = a - mean[c][r];
-        mean[c][r] = fmaf(d, inv_n, mean[c][r]);
-        m2[c][r] = fmaf(d, a - mean[c][r], m2[c][r]);
+        if constexpr (FIRST) {
+          a0[c][r] = a;
+        } else {
+          const float d = a - a0[c][r];
+          s1[c][r] += d;
+          s2[c][r] = fmaf(d, d, s2[c][r]);
+        }
       }
     alogA += (double)alog;
     if (more) {
@@ -267,10 +276,22 @@ __global__ __launch_bounds__(256) void calib_stats_kernel(CalibArgs A) {
     }
     __syncthreads();
   };
-  if (nomask)
-    for (int n = 0; n < A.N; ++n) step(std::false_type{}, n);
-  else
-    for (int n = 0; n < A.N; ++n) step(std::true_type{}, n);
+  if (nomask) {
+    step(std::false_type{}, std::true_type{}, 0);
+    for (int n = 1; n < A.N; ++n) step(std::false_type{}, std::false_type{}, n);
+  } else {
+    step(std::true_type{}, std::true_type{}, 0);
+    for (int n = 1; n < A.N; ++n) step(std::true_type{}, std::false_type{}, n);
+  }
+  const float invN = 1.f / (float)A.N;
+  f32x16 mean[2], m2[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      mean[c][r] = fmaf(s1[c][r], invN, a0[c][r]);
+      m2[c][r] = fmaf(-s1[c][r], s1[c][r] * invN, s2[c][r]);
+    }
 
   // store the mean of the causal entries; sums for the scores
   double sm2 = 0.0, shat = 0.0;

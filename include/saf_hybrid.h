@@ -310,10 +310,10 @@ size_t saf_fit_pattern_workspace_bytes(int32_t n_heads, int32_t T);
  *   s_var[h] = sum_n sum_{i,j} (A^(n)[i][j] - ahat[i][j])^2 / ((N - 1) T^2)
  *              (0 when N = 1)
  *   s_kl[h]  = (N T)^-1 sum_n sum_i KL(A^(n)[i][0..i] || ahat[i][0..i])
- * in one pass over the sequences without storing any A^(n): the running
- * mean and squared deviations of every entry (Welford's update) are kept
- * on chip, and the KL sum uses sum_n KL = sum_n sum A ln A - N sum
- * ahat ln ahat.  Entries above the diagonal of ahat are not written.
+ * in one pass over the sequences without storing any A^(n): every entry's
+ * sums of deviations from its first sequence's value are kept on chip
+ * (mean and squared deviations follow from them), and the KL sum uses
+ * sum_n KL = sum_n sum A ln A - N sum ahat ln ahat.  Entries above the diagonal of ahat are not written.
  *   q, k        : device bf16 [N][H][T][D] with element strides
  *                 (sequence, head, row) in q_stride / k_stride; last
  *                 dimension contiguous; 16-byte aligned, strides multiples

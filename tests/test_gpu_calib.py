@@ -8,12 +8,15 @@ subtracts the row's log-sum-exp, itself a sum of at most T terms in fp32
 (relative error (T + 2) u, i.e. (T + 2) u / ln 2 in log2 units).  So every
 probability carries a relative error of at most
     rho = ln 2 (2 sl2 D u max|q.k|_1 + 2 u max|x|) + (T + 4) u + 2^-21
-(x the log2 probability, 2^-21 for the hardware exp2), and the running mean
-over N sequences adds N u.  The mean is compared entry by entry at
-rho + N u relative.  s_var sums each entry's squared deviations: a relative
-error rho on every probability moves it by at most
-2 rho sum_n sum |A_n - A-hat| A_n, plus 4 N u sum A_n^2 for the fp32
-Welford updates.  s_KL is sum_n sum A ln A - N sum A-hat ln A-hat: each term
+(x the log2 probability, 2^-21 for the hardware exp2), and the mean over N
+sequences (A0 + s1/N from the shifted sums s1 = sum (A - A0), s2 =
+sum (A - A0)^2, A0 the first sequence's value) adds N u.  The mean is
+compared entry by entry at rho + N u relative.  s_var sums each entry's
+squared deviations s2 - s1^2/N: a relative error rho on every probability
+moves it by at most 2 rho sum_n sum |A_n - A-hat| A_n; the fp32 sums add at
+most N u s2 (s2), and 2 u (sum |A - A0|)^2 <= 2 N u s2 (s1^2/N), so
+3 N u sum_n sum (A_n - A0)^2 in all, plus 4 u sum A_n^2 for the final
+subtraction and the fp64 partial sums.  s_KL is sum_n sum A ln A - N sum A-hat ln A-hat: each term
 moves by (rho + 64 u) A (|ln A| + 1) at most (64 u for the fp32 sums of a
 lane's terms before they join the fp64 partials).
 """
@@ -69,13 +72,14 @@ def _sums(q, k, scale, rows):
 
     return {"ahat": Ah, "sq": part["sq"], "kl": part["kl"],
             "dev": float((np.abs(As - Ah[None]) * As).sum()), "sq_all": float((As ** 2).sum()),
+            "sq_shift": float(((As - As[:1]) ** 2).sum()),
             "ent": sum(alnA(As[n]) for n in range(N)) + N * alnA(Ah)}
 
 
 def _score_bars(rho, N, T, tot):
     var_bar = 0.0
     if N > 1:
-        var_bar = (2 * rho * tot["dev"] + 4 * N * U * tot["sq_all"]) / ((N - 1) * T * T)
+        var_bar = (2 * rho * tot["dev"] + 3 * N * U * tot["sq_shift"] + 4 * U * tot["sq_all"]) / ((N - 1) * T * T)
     kl_bar = (rho + 64 * U) * tot["ent"] / (N * T)
     return var_bar, kl_bar
 
@@ -188,7 +192,7 @@ def test_calib_workload_sampled(B):
         tot = None
         for r0 in range(0, T, 512):
             part = _sums(qh, kh, scale, np.arange(r0, min(r0 + 512, T)))
-            tot = part if tot is None else {x: tot[x] + part[x] for x in ("sq", "kl", "dev", "sq_all", "ent")}
+            tot = part if tot is None else {x: tot[x] + part[x] for x in ("sq", "kl", "dev", "sq_all", "sq_shift", "ent")}
         ref_var = tot["sq"] / ((N - 1) * T * T)
         ref_kl = tot["kl"] / (N * T)
         var_bar, kl_bar = _score_bars(_rho(qh, kh, scale, T, D), N, T, tot)
