@@ -200,3 +200,14 @@ def test_calib_workload_sampled(B):
             f"s_kl {s_kl[h]:.6e} vs {ref_kl:.6e} (bar {kl_bar:.1e})")
         assert abs(s_var[h] - ref_var) <= var_bar
         assert abs(s_kl[h] - ref_kl) <= kl_bar
+
+
+def test_calib_many_heads(B):
+    """300 heads (more than a head list holds) of a short sequence."""
+    N, H, T, D = 2, 300, 40, 64
+    q, k = calibration_qk(N, H, T, D, seed=77)
+    ahat, s_var, s_kl = B.saf_calib_stats(_dev(q), _dev(k))
+    torch.cuda.synchronize()
+    ahat, s_var, s_kl = host(ahat), s_var.cpu().numpy(), s_kl.cpu().numpy()
+    for h in (0, 256, H - 1):
+        _check_head(q[:, h], k[:, h], 1 / math.sqrt(D), ahat[h], s_var[h], s_kl[h], f"many heads: head {h}")

@@ -343,3 +343,14 @@ def test_fit_workload_sampled(B):
         assert dks <= KAPPA_SELF_ABS
         assert dzs <= LSE_FRZ_ABS
         assert red < 0.1
+
+
+def test_fit_many_heads(B):
+    """More heads than a head list holds (300): the fit indexes heads by grid
+    position; three heads checked over the first steps and at init."""
+    n, T = 300, 64
+    A = np.stack([calibration_mean(T, 606, h) for h in range(n)])
+    ea, er, ne = _fit_inputs(A)
+    g = _run_fit(B, ea, er, ne, 3)
+    for h in (0, 257, n - 1):
+        _check_steps(g, h, ea[h], er[h], 3, f"many heads: head {h}")

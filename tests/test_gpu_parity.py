@@ -359,6 +359,33 @@ def test_workload_prefill_32k_sampled_rows(B):
     assert e <= LSE_FRZ_ABS
 
 
+@pytest.mark.parametrize("T", [8193, 16385])
+def test_forward_normaliser_key_groups(B, T):
+    """Normaliser partials over key groups of 512 (T = 8193: two chunks of
+    256 keys per group) and 768 (T = 16385: three chunks) keys; sampled rows
+    of both head kinds and log N of the frozen head."""
+    cfg = CONFIGS["pages_check_t129"].with_(T=T, B=1, H=2, frozen=(1,), prior_len=None, bwd=False,
+                                            name=f"keygroups_T{T}")
+    say(f"case {cfg.name}")
+    inp = make_inputs(cfg, with_do=False)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 511, 512, 767, 768, 1023, 1024, T - 2, T - 1],
+                                     np.random.default_rng(T).integers(0, T, 30)]))
+    s = 1.0 / np.sqrt(cfg.D)
+    ro, rl = oracle.ordinary_rows_fwd(inp.q[0, 0], inp.k[0, 0], inp.v[0, 0], s, rows)
+    _check_head("h0 rows", cfg, host(O[0, 0])[rows], ro, host(L[0, 0])[rows], rl, 0)
+    ro, rl = oracle.frozen_rows_fwd(inp.v[0, 1], inp.a[1], inp.r[1], rows)
+    _check_head("h1 rows", cfg, host(O[0, 1])[rows], ro, host(L[0, 1])[rows], rl, 1)
+    rows = np.arange(0, T, 97)
+    rl = oracle.frozen_rows_fwd(np.zeros((T, 1)), inp.a[1], inp.r[1], rows)[1]
+    e = max_abs(host(L[0, 1])[rows], rl)
+    say(f"  h1 log N on {len(rows)} rows max-abs {e:.3e}")
+    assert e <= LSE_FRZ_ABS
+
+
 # --------------------------------------------------------------------------
 # Grouped-query forward (key/value heads shared by groups of query heads)
 # --------------------------------------------------------------------------
