@@ -176,6 +176,8 @@ constexpr int kWaves = SAF_FIT_WAVES;  // waves per block, splitting each chunk
 constexpr int kNT = 64 * kWaves;
 constexpr int kOut = 64 * kQ;         // parameters per step block
 constexpr int kTK = 256;              // summation indices per chunk
+constexpr int kWaveSpan = kTK / kWaves;  // summation indices per wave and chunk
+static_assert(kWaveSpan % 4 == 0, "waves sum whole groups of four");
 constexpr int kBand = kOut + kTK - 1; // band entries a chunk touches
 constexpr int kBandPad = kBand + 1;   // one zero entry past the end
 static_assert(kBandPad % 4 == 0, "band rows are read 16 bytes at a time");
@@ -229,8 +231,9 @@ __device__ __forceinline__ void lse_merge(float& M, float& S, float cm, float cs
 //     Y[y] = r2[offset].
 // So y = SX x + SO (4L + q) + OFF, and the seven entries a lane needs for a
 // group x..x+3 start at yb = SX x + SO 4L + OFFB, a multiple of four: two
-// aligned 16-byte reads for sixteen products.  Entries outside [0, T) are
-// -inf (their exponentials 0).
+// aligned 16-byte reads.  A wave sums a contiguous range of a chunk, so the
+// next group's window shares one of those reads: one new 16-byte read per
+// sixteen products.  Entries outside [0, T) are -inf (their exponentials 0).
 template <int KIND>
 struct BandKind {
   static constexpr int SX = KIND == 2 ? -1 : 1;
@@ -264,54 +267,73 @@ __device__ __forceinline__ float band_val(float raw, bool ok, bool negate) {
   return ok ? (negate ? -raw : raw) * kLog2e : kNegInf;
 }
 
-// Exact max-shifted sum of one output's terms over a wave's groups of a
-// chunk (x = g .. g+3 for g = xq, xq + 4 kWaves, ... up to xlast; band index
-// SX x + yq), as a (max, sum) pair in log2 units.  Rarely taken, so kept out
-// of line: the summing loop keeps its registers.
+// Exact max-shifted sum of one output's terms over a wave's range of a
+// chunk (x = xq .. xend; band index SX x + yq), as a (max, sum) pair in log2
+// units.  Rarely taken, so kept out of line: the summing loop keeps its
+// registers.
 __device__ __attribute__((noinline)) float2 exact_chunk_sum(const float* x2, const float* y2, int sx, int yq,
-                                                            int xq, int xlast) {
+                                                            int xq, int xend) {
   float cm = kNegInf;
-  for (int g = xq; g <= xlast; g += 4 * kWaves)
-    for (int x = g; x < g + 4 && x <= xlast; ++x) cm = fmaxf(cm, x2[x] + y2[sx * x + yq]);
+  for (int x = xq; x <= xend; ++x) cm = fmaxf(cm, x2[x] + y2[sx * x + yq]);
   float cs = 0.f;
   if (cm != kNegInf)
-    for (int g = xq; g <= xlast; g += 4 * kWaves)
-      for (int x = g; x < g + 4 && x <= xlast; ++x) cs += fast_exp2(x2[x] + y2[sx * x + yq] - cm);
+    for (int x = xq; x <= xend; ++x) cs += fast_exp2(x2[x] + y2[sx * x + yq] - cm);
   return make_float2(cm, cs);
 }
 
-// Whether any of a wave's summation indices (x with x mod 16 in [xq, xq+3],
-// 0 <= x <= xlast) falls in output o's causal range for the chunk at c0:
+// Whether any of a wave's summation indices (xq <= x <= xend) falls in
+// output o's causal range for the chunk at c0:
 //   kind 0 (output k): rows i = c0 + x with k <= i < T;
 //   kind 1 (output d): keys k = c0 + x with 0 <= k < T - d;
 //   kind 2 (output i): keys k = c0 + x with 0 <= k <= i.
 // Terms in that range are finite (a, r and log N are), so a zero sum with
 // no such index is exact and needs no recomputation.
 template <int KIND>
-__device__ __forceinline__ bool wave_has_terms(int o, int c0, int xq, int xlast, int T) {
-  int lo = KIND == 0 ? o - c0 : -c0;
-  int hi = KIND == 0 ? T - 1 - c0 : (KIND == 1 ? T - 1 - o - c0 : o - c0);
-  lo = max(lo, 0);
-  hi = min(hi, xlast);
-  if (lo > hi) return false;
-  const int period = 4 * kWaves;
-  const int r = lo % period;
-  const int first = r < xq ? lo - r + xq : (r <= xq + 3 ? lo : lo - r + period + xq);
-  return first <= hi;
+__device__ __forceinline__ bool wave_has_terms(int o, int c0, int xq, int xend, int T) {
+  const int lo = KIND == 0 ? o - c0 : -c0;
+  const int hi = KIND == 0 ? T - 1 - c0 : (KIND == 1 ? T - 1 - o - c0 : o - c0);
+  return max(lo, xq) <= min(hi, xend);
 }
 
-// Sixteen products of one group of four summation indices.
+// Sixteen products of one group of four summation indices; ya and yc hold
+// band entries yb..yb+3 and yb+4..yb+7.
 template <int KIND>
-__device__ __forceinline__ void group_fma(const lds_f32* xe, const lds_f32* ye, int x, int yb, float* s) {
+__device__ __forceinline__ void group_fma(const f32x4& e4, const f32x4& ya, const f32x4& yc, float* s) {
   using K = BandKind<KIND>;
-  const f32x4 e4 = lds_read_f4(xe + x);
-  const f32x4 ya = lds_read_f4(ye + yb);
-  const f32x4 yc = lds_read_f4(ye + (yb + 4));
   const float yv[8] = {ya[0], ya[1], ya[2], ya[3], yc[0], yc[1], yc[2], yc[3]};
 #pragma unroll
   for (int q = 0; q < kQ; ++q)
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[q] = fmaf(e4[e], yv[K::idx(q, e)], s[q]);
+}
+
+// Products of the groups starting at x, x + 4, ... (ng of them): each step
+// moves the band window by SX * 4 entries, so one half of it is carried
+// over and the other read.
+template <int KIND, bool UNROLL>
+__device__ __forceinline__ void range_fma(const lds_f32* xe, const lds_f32* ye, int x, int ng, int yb, float* s) {
+  using K = BandKind<KIND>;
+  f32x4 ya = lds_read_f4(ye + yb);
+  f32x4 yc = lds_read_f4(ye + (yb + 4));
+  auto step = [&](int u) {
+    if (u > 0) {
+      if (K::SX > 0) {
+        ya = yc;
+        yc = lds_read_f4(ye + (yb + 4 * u + 4));
+      } else {
+        yc = ya;
+        ya = lds_read_f4(ye + (yb - 4 * u));
+      }
+    }
+    group_fma<KIND>(lds_read_f4(xe + (x + 4 * u)), ya, yc, s);
+  };
+  if constexpr (UNROLL) {
+#pragma unroll
+    for (int u = 0; u < kWaveSpan / 4; ++u) step(u);
+  } else {
+#pragma unroll 2
+    for (int u = 0; u < ng; ++u) step(u);
+  }
 }
 
 // Summation range of an output block (chunks of kTK from cbeg to cend):
@@ -422,26 +444,22 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0, int
     // finished the chunk before the last, which used the other buffer
     __syncthreads();
 
-    // x past the summation range has a zero factor on one side, so every
-    // lane runs the same loop
+    // wave w sums x in [xq, xend], a contiguous quarter of the chunk; x past
+    // the summation range has a zero factor on one side, so every lane runs
+    // the same loop
     const int xlast = min(kTK, cend - c0) - 1;
-    const int xq = 4 * __builtin_amdgcn_readfirstlane(w);
+    const int xq = kWaveSpan * __builtin_amdgcn_readfirstlane(w);
+    const int xend = min(xq + kWaveSpan - 1, xlast);
     const int ybl = K::SO * kQ * lane + K::OFFB;  // yb - SX x
     if (xq <= xlast && ol < T) {
       const lds_f32* xe = (const lds_f32*)sb.xe;
       const lds_f32* ye = (const lds_f32*)sb.ye;
       float s[kQ] = {0.f, 0.f, 0.f, 0.f};
-      constexpr int kGroups = kTK / (4 * kWaves);  // groups of a full chunk per wave
-      if (xlast == kTK - 1) {
-        // full chunk: straight-line code, so reads can be issued ahead
-#pragma unroll
-        for (int u = 0; u < kGroups; ++u) {
-          const int x = xq + 4 * kWaves * u;
-          group_fma<KIND>(xe, ye, x, K::SX * x + ybl, s);
-        }
+      if (xend == xq + kWaveSpan - 1) {
+        // the whole range: straight-line code, so reads can be issued ahead
+        range_fma<KIND, true>(xe, ye, xq, kWaveSpan / 4, K::SX * xq + ybl, s);
       } else {
-#pragma unroll 2
-        for (int x = xq; x <= xlast; x += 4 * kWaves) group_fma<KIND>(xe, ye, x, K::SX * x + ybl, s);
+        range_fma<KIND, false>(xe, ye, xq, (xend - xq) / 4 + 1, K::SX * xq + ybl, s);
       }
 #pragma unroll
       for (int q = 0; q < kQ; ++q) {
@@ -451,8 +469,8 @@ __device__ void band_sums(const FitStepArgs& A, StepSmem& sm, int h, int o0, int
         // terms stay below 2^-120, which is 2^-24 of any sum >= 2^-96
         if (s[q] >= 0x1p-96f) {
           lse_merge(M[q], S[q], mx + my, s[q]);
-        } else if (wave_has_terms<KIND>(ol + q, c0, xq, xlast, T)) {
-          const float2 ex = exact_chunk_sum(sb.x2, sb.y2, K::SX, K::SO * (kQ * lane + q) + K::OFF, xq, xlast);
+        } else if (wave_has_terms<KIND>(ol + q, c0, xq, xend, T)) {
+          const float2 ex = exact_chunk_sum(sb.x2, sb.y2, K::SX, K::SO * (kQ * lane + q) + K::OFF, xq, xend);
           lse_merge(M[q], S[q], ex.x, ex.y);
         }
       }
