@@ -516,7 +516,7 @@ def main():
                     help="only run a plain copy of known size (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is not built "
+        print(json.dumps({"error": "this library runs on one GPU only; multi-GPU sharding is not built "
                                    "(--gpus must be 1)"}))
         sys.exit(2)
 
