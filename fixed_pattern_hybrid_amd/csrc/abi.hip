@@ -450,7 +450,7 @@ bool fit_sizes_ok(int32_t n_heads, int32_t T) {
 size_t fit_targets_ws(int32_t n_heads, int32_t T) {
   const size_t nT = (size_t)n_heads * (size_t)T;
   const size_t nseg = ((size_t)T + saf::kFitSegRows - 1) / saf::kFitSegRows;
-  return 2 * round_up(nT * sizeof(float), 256) + round_up(nT * 2 * nseg * sizeof(float), 256);
+  return 2 * round_up(nT * sizeof(float), 256) + round_up(nT * 5 * nseg * sizeof(float), 256);
 }
 
 size_t fit_maxg(int32_t T) {

@@ -8,11 +8,16 @@
 //                     reads T+1 causal entries: the row sum s_i of the
 //                     entries floored at `floor`, and the row's
 //                     sum_j p log p for p = floored / s_i.
-//   fit_tmarg_kernel  one thread per column (kind 0) or per diagonal
-//                     (kind 1), looping over a segment of kSeg rows: the
-//                     diagonal d's entry in row i is column i - d, so both
-//                     kinds read a contiguous run of each row.  Per-segment
-//                     partial sums go to the workspace.
+//   fit_cmarg4_kernel / fit_dmarg4_kernel  (rows 16-byte aligned) column
+//                     and diagonal sums with 16-byte reads over segments of
+//                     kSeg rows: a thread owns four columns, or reads the
+//                     aligned run (i, 4(m - k) .. +3) of rows i = 4m + u,
+//                     whose entries lie on four fixed diagonals.
+//   fit_tmarg_kernel  (other layouts) one thread per column (kind 0) or per
+//                     diagonal (kind 1), reading 4 bytes per row.
+//   Per-segment partial sums go to the workspace, [h][seg][5][T]: slot 0
+//   the column sums, slots 1..4 the diagonal sums (one slot per run
+//   position e in the aligned kernel, slot 1 alone otherwise).
 //   fit_tred_kernel   fixed-order sums of the segment partials (eta_abs,
 //                     eta_rel); fit_negent_kernel sums the row entropies.
 //
@@ -48,6 +53,7 @@ namespace {
 constexpr int kRowWaves = 4;
 constexpr int kTChunk = 256;  // outputs (columns or diagonals) per marginal block
 constexpr int kSeg = kFitSegRows;
+constexpr int kPartSlots = 5;  // partial-sum slots per segment: columns, four diagonal slots
 
 __device__ __forceinline__ float wave_sum(float v) {
   // butterfly in a fixed order: every lane ends with the same value
@@ -124,23 +130,112 @@ __global__ __launch_bounds__(kTChunk) void fit_tmarg_kernel(FitTargetArgs A) {
       acc = fmaf(fmaxf(base[(int64_t)i * A.row_stride + col], fl), inv, acc);
     }
   }
-  if (o < T) A.part[(((int64_t)h * 2 + kind) * A.nseg + seg) * T + o] = acc;
+  if (o < T) A.part[(((int64_t)h * A.nseg + seg) * kPartSlots + kind) * T + o] = acc;
 }
 
-__global__ __launch_bounds__(kTChunk) void fit_tred_kernel(FitTargetArgs A) {
+// Column sums with 16-byte reads: thread t owns columns o .. o+3, o = 1024
+// blockIdx.x + 4t, and sums rows [max(seg start, o), seg end).  Every
+// thread writes its slot-0 partials, zero where it has no rows.
+__global__ __launch_bounds__(kTChunk) void fit_cmarg4_kernel(FitTargetArgs A) {
+  const int T = A.T;
+  const int h = blockIdx.z, seg = blockIdx.y;
+  const int c0 = blockIdx.x * 4 * kTChunk;
+  const int o = c0 + 4 * (int)threadIdx.x;
+  const int rb = max(c0, seg * kSeg), re = min((seg + 1) * kSeg, T);
+  const float fl = A.floor;
+  const float* base = A.ahat + (int64_t)h * A.head_stride;
+  const float* inv_s = A.inv_s + (int64_t)h * T;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  // rows i >= o + 3, where the whole run is causal and inside [0, T): every
+  // lane runs the same loop, lanes without such a row reading column 0
+  // (a valid address) and discarding it
+#pragma unroll 4
+  for (int i = rb; i < re; ++i) {
+    const bool ok = i >= o + 3;
+    const float inv = inv_s[i];
+    const f32x4 x = *reinterpret_cast<const f32x4*>(base + (int64_t)i * A.row_stride + (ok ? o : 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = ok ? fmaf(fmaxf(x[e], fl), inv, acc[e]) : acc[e];
+  }
+  // rows o .. o+2 cross the diagonal
+  for (int i = max(o, rb); i < min(o + 3, re); ++i) {
+    const float inv = inv_s[i];
+    const float* row = base + (int64_t)i * A.row_stride;
+    for (int e = 0; e <= i - o; ++e) acc[e] = fmaf(fmaxf(row[o + e], fl), inv, acc[e]);
+  }
+  float* out = A.part + ((int64_t)h * A.nseg + seg) * kPartSlots * T;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (o + e < T) out[o + e] = acc[e];
+}
+
+// Diagonal sums with 16-byte reads.  Wave u reads rows i = 4m + u; lane L
+// owns k = 64 blockIdx.x + L and reads the aligned run (i, 4(m-k) .. +3)
+// for m >= k.  Entry e of the run lies on diagonal d = 4k + u - e, and its
+// sum over the segment goes to slot 1 + e of d.  A (slot, diagonal) pair
+// has one owner, k = floor((d + e) / 4), u = (d + e) mod 4, whose rows are
+// all >= d.  Every owner writes its partials, zero where it has no rows.
+__global__ __launch_bounds__(kTChunk) void fit_dmarg4_kernel(FitTargetArgs A) {
+  const int T = A.T;
+  const int h = blockIdx.z, seg = blockIdx.y;
+  const int u = __builtin_amdgcn_readfirstlane(wave_id());
+  const int k = 64 * blockIdx.x + lane_id();
+  const int ilo = seg * kSeg, ihi = min((seg + 1) * kSeg, T);
+  // m with ilo <= 4m + u < ihi
+  const int mb = ilo - u <= 0 ? 0 : (ilo - u + 3) / 4;
+  const int me = ihi - u <= 0 ? 0 : (ihi - u + 3) / 4;
+  const float fl = A.floor;
+  const float* base = A.ahat + (int64_t)h * A.head_stride;
+  const float* inv_s = A.inv_s + (int64_t)h * T;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int m0 = max(mb, 64 * (int)blockIdx.x);  // no lane has rows before this
+  // k >= 1: columns 4(m-k) .. 4(m-k)+3 < 4m <= i are causal and inside the
+  // row.  Every lane runs the same loop; a lane with m < k (or k = 0) reads
+  // column 0 (a valid address) and discards it.
+#pragma unroll 4
+  for (int m = m0; m < me; ++m) {
+    const bool ok = m >= k && k > 0;
+    const int i = 4 * m + u;
+    const float inv = inv_s[i];
+    const f32x4 x =
+        *reinterpret_cast<const f32x4*>(base + (int64_t)i * A.row_stride + (ok ? 4 * (m - k) : 0));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = ok ? fmaf(fmaxf(x[e], fl), inv, acc[e]) : acc[e];
+  }
+  // k = 0: the run (i, 4m .. 4m+3) crosses the diagonal; entries e <= u
+  if (k == 0) {
+    for (int m = mb; m < me; ++m) {
+      const int i = 4 * m + u;
+      const float inv = inv_s[i];
+      const float* run = base + (int64_t)i * A.row_stride + 4 * m;
+      for (int e = 0; e <= u; ++e) acc[e] = fmaf(fmaxf(run[e], fl), inv, acc[e]);
+    }
+  }
+  float* out = A.part + ((int64_t)h * A.nseg + seg) * kPartSlots * T;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int d = 4 * k + u - e;
+    if (d >= 0 && d < T) out[(int64_t)(1 + e) * T + d] = acc[e];
+  }
+}
+
+// rel_slots: diagonal slots the marginal kernels wrote (4 aligned, else 1).
+__global__ __launch_bounds__(kTChunk) void fit_tred_kernel(FitTargetArgs A, int rel_slots) {
   const int T = A.T;
   const int h = blockIdx.y;
   const int c0 = blockIdx.x * kTChunk;
   const int o = c0 + (int)threadIdx.x;
   if (o >= T) return;
   const int s0 = c0 / kSeg;  // first segment holding rows >= c0
-#pragma unroll
-  for (int kind = 0; kind < 2; ++kind) {
-    const float* pp = A.part + ((int64_t)h * 2 + kind) * A.nseg * T + o;
-    float acc = 0.f;
-    for (int s = s0; s < A.nseg; ++s) acc += pp[(int64_t)s * T];
-    (kind == 0 ? A.eta_abs : A.eta_rel)[(int64_t)h * T + o] = acc;
+  const float* pp = A.part + (int64_t)h * A.nseg * kPartSlots * T + o;
+  float ca = 0.f, cr = 0.f;
+  for (int s = s0; s < A.nseg; ++s) {
+    const float* ps = pp + (int64_t)s * kPartSlots * T;
+    ca += ps[0];
+    for (int e = 0; e < rel_slots; ++e) cr += ps[(int64_t)(1 + e) * T];
   }
+  A.eta_abs[(int64_t)h * T + o] = ca;
+  A.eta_rel[(int64_t)h * T + o] = cr;
 }
 
 // Fixed-order double sum of x[0..n) over one block of 256 threads.
@@ -659,9 +754,21 @@ hipError_t launch_fit_targets(const FitTargetArgs& args, hipStream_t stream) {
   hipLaunchKernelGGL(fit_rows_kernel, dim3((npairs + kRowWaves - 1) / kRowWaves, args.n_heads),
                      dim3(64 * kRowWaves), 0, stream, args);
   const int nchunk = (T + kTChunk - 1) / kTChunk;
-  hipLaunchKernelGGL(fit_tmarg_kernel, dim3(nchunk, args.nseg, 2 * args.n_heads), dim3(kTChunk), 0,
-                     stream, args);
-  hipLaunchKernelGGL(fit_tred_kernel, dim3(nchunk, args.n_heads), dim3(kTChunk), 0, stream, args);
+  // every row starts 16-byte aligned (and has the four columns that lanes
+  // without work read): the 16-byte-read kernels
+  const bool vec = (reinterpret_cast<uintptr_t>(args.ahat) & 15) == 0 && args.row_stride % 4 == 0 &&
+                   args.head_stride % 4 == 0 && T >= 4;
+  if (vec) {
+    const int nk = (T + 2) / 4 + 1;  // k of every (slot, diagonal) owner
+    hipLaunchKernelGGL(fit_cmarg4_kernel, dim3((T + 4 * kTChunk - 1) / (4 * kTChunk), args.nseg, args.n_heads),
+                       dim3(kTChunk), 0, stream, args);
+    hipLaunchKernelGGL(fit_dmarg4_kernel, dim3((nk + 63) / 64, args.nseg, args.n_heads), dim3(kTChunk), 0,
+                       stream, args);
+  } else {
+    hipLaunchKernelGGL(fit_tmarg_kernel, dim3(nchunk, args.nseg, 2 * args.n_heads), dim3(kTChunk), 0,
+                       stream, args);
+  }
+  hipLaunchKernelGGL(fit_tred_kernel, dim3(nchunk, args.n_heads), dim3(kTChunk), 0, stream, args, vec ? 4 : 1);
   hipLaunchKernelGGL(fit_negent_kernel, dim3(args.n_heads), dim3(256), 0, stream, args);
   return hipGetLastError();
 }

@@ -142,7 +142,7 @@ struct FitTargetArgs {
   int n_heads, T, nseg;
   float* inv_s;         // workspace [n][T]: 1 / row sum of the floored entries
   float* row_ent;       // workspace [n][T]: sum_j p log p of each row
-  float* part;          // workspace [n][2][nseg][T]: segment partial marginals
+  float* part;          // workspace [n][nseg][5][T]: segment partial marginals
   float* eta_abs;       // [n][T] output
   float* eta_rel;       // [n][T] output
   float* negent;        // [n] output

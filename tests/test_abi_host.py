@@ -329,8 +329,8 @@ def test_fit_workspace_sizes(b):
     assert L.saf_fit_targets_workspace_bytes(3, 0) == 0
     assert L.saf_fit_targets_workspace_bytes(16385, 10) == 0
     # row sums and entropies [n][T], partial marginals [n][2][ceil(T/512)][T]
-    assert L.saf_fit_targets_workspace_bytes(3, 1000) == 2 * _ru(3000 * 4) + _ru(3000 * 2 * 2 * 4)
-    assert L.saf_fit_targets_workspace_bytes(36, 4096) == 2 * _ru(36 * 4096 * 4) + _ru(36 * 4096 * 2 * 8 * 4)
+    assert L.saf_fit_targets_workspace_bytes(3, 1000) == 2 * _ru(3000 * 4) + _ru(3000 * 5 * 2 * 4)
+    assert L.saf_fit_targets_workspace_bytes(36, 4096) == 2 * _ru(36 * 4096 * 4) + _ru(36 * 4096 * 5 * 8 * 4)
     # second parameter buffer and four moment vectors, five arrays of
     # 256-entry segment maxima (a and r of both buffers, -log N), then float2
     # partials of chunk groups (4 chunks of 256) for the normalisers and both

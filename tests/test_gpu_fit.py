@@ -120,6 +120,26 @@ def test_fit_targets_upper_triangle_strides_and_floor(B):
     assert torch.equal(one[0][0], base[0][0]) and torch.equal(one[2][0], base[2][0])
 
 
+@pytest.mark.parametrize("T", [256, 300, 1024])
+def test_fit_targets_vector_and_scalar_reads(B, T):
+    """Rows that start 16-byte aligned take the 16-byte-read marginal
+    kernels, other layouts the 4-byte ones: a tensor and its copy with rows
+    padded to an odd stride both match the oracle."""
+    n = 2
+    A = _means(n, T, 40 + T)
+    aligned = torch.from_numpy(A).cuda()
+    pad = np.zeros((n, T, T + 1), dtype=np.float32)
+    pad[:, :, :T] = A
+    odd = torch.from_numpy(pad).cuda()[:, :, :T]
+    got_a = B.saf_fit_targets(aligned)
+    got_o = B.saf_fit_targets(odd)
+    torch.cuda.synchronize()
+    for h in range(n):
+        ref = F.fit_statistics(A[h])
+        for got, what in ((got_a, "16-byte"), (got_o, "4-byte")):
+            _check_stats(T, host(got[0])[h], host(got[1])[h], host(got[2])[h], ref, f"{what} reads T={T} head {h}")
+
+
 def test_fit_targets_deterministic(B):
     A = torch.from_numpy(_means(2, 700, 9)).cuda()
     x = B.saf_fit_targets(A)
