@@ -21,15 +21,19 @@
 //   fit_tred_kernel   fixed-order sums of the segment partials (eta_abs,
 //                     eta_rel); fit_negent_kernel sums the row entropies.
 //
-// The fit (two launches per Adam step), both one band-sum program with
-// 256 outputs per block (four per lane):
-//   fit_norm_kernel  log N(i) of the current (a, r) (Equation 3);
-//   fit_step_kernel  the fitted marginals
+// The fit (four launches per Adam step).  Two run one band-sum program with
+// 256 outputs per block (four per lane), over groups of at most
+// kFitGroupChunks chunks, writing (max, sum) partials; two merge them:
+//   fit_norm_part_kernel + fit_norm_merge_kernel  log N(i) of the current
+//     (a, r) (Equation 3) and the segment maxima of -log N;
+//   fit_marg_part_kernel + fit_update_kernel  the fitted marginals
 //     mu_abs(k) = exp(a_k) * sum_{i >= k} exp(r_{i-k} - z_i)
 //     mu_rel(d) = exp(r_d) * sum_{k < T-d} exp(a_k - z_{k+d})
 //   (kind 0 = a, kind 1 = r), the gradient (mu - eta) / T (Equation 20) and
 //   the Adam update, written to the other of two parameter buffers so that
 //   every block of a step reads the same point.
+// The forward's normaliser of frozen heads (norm_segmax_kernel, then the
+// same fit_norm_part_kernel) reuses the normaliser kind.
 //
 // The sums factor like the forward's normaliser: over a chunk of kTK
 // summation indices, exp2(X[x] + Y[y]) = 2^(mx + my) exp2(X[x] - mx)
