@@ -140,6 +140,24 @@ def test_fit_targets_vector_and_scalar_reads(B, T):
             _check_stats(T, host(got[0])[h], host(got[1])[h], host(got[2])[h], ref, f"{what} reads T={T} head {h}")
 
 
+def test_fit_targets_head_stride_off_alignment(B):
+    """Rows 16-byte aligned within each head but heads 8 bytes apart from a
+    16-byte boundary: the 4-byte-read kernels run, and every head matches
+    the oracle and the same means stored contiguously."""
+    T, n = 256, 3
+    A = _means(n, T, 77)
+    flat = torch.zeros(n * (T * T + 2), dtype=torch.float32, device="cuda")
+    view = flat.as_strided((n, T, T), (T * T + 2, T, 1))
+    view.copy_(torch.from_numpy(A).cuda())
+    got = B.saf_fit_targets(view)
+    dense = B.saf_fit_targets(torch.from_numpy(A).cuda())
+    torch.cuda.synchronize()
+    for h in range(n):
+        ref = F.fit_statistics(A[h])
+        _check_stats(T, host(got[0])[h], host(got[1])[h], host(got[2])[h], ref, f"head stride T*T+2, head {h}")
+        _check_stats(T, host(dense[0])[h], host(dense[1])[h], host(dense[2])[h], ref, f"contiguous, head {h}")
+
+
 def test_fit_targets_deterministic(B):
     A = torch.from_numpy(_means(2, 700, 9)).cuda()
     x = B.saf_fit_targets(A)
