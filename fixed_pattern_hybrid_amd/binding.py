@@ -71,6 +71,7 @@ class SafParams(ctypes.Structure):
         ("n_stage_events", ctypes.c_int32),
         ("kv_heads", ctypes.c_int32),
         ("logz", ctypes.c_void_p),
+        ("qk_packed", ctypes.c_int32),
     ]
 
 
@@ -246,8 +247,55 @@ def workspace_bytes(params: Params, for_bwd: bool) -> int:
     return int(LIB.saf_hybrid_attn_workspace_bytes(params.ref(), 1 if for_bwd else 0))
 
 
+def _n_ordinary(frozen) -> int:
+    return len(frozen) - sum(int(x) for x in frozen)
+
+
+def _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz):
+    """saf_hybrid_attn_fwd with q (and k, for multi-head K/V) holding only
+    the ordinary heads, in increasing head order."""
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a [B, Hkv, T, D] tensor")
+    H, n_ord = len(frozen), _n_ordinary(frozen)
+    B, Hkv, T, D = v.shape
+    if Hkv < 1 or H % Hkv != 0:
+        raise ValueError(f"v has {Hkv} heads, which must divide the {H} heads of the frozen mask")
+    if out is None:
+        out = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
+    _check_layer_inputs(out, a, r)
+    _check_like("v", v, out, shape=(B, Hkv, T, D))
+    if n_ord > 0:
+        _check_like("q", q, out, shape=(B, n_ord, T, D))
+        _check_like("k", k, out, shape=(B, n_ord if Hkv == H else Hkv, T, D))
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    _check_like("lse", lse, out, shape=(B, H, T), dtype=torch.float32)
+    if not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, T]")
+    if logz is not None:
+        _check_like("logz", logz, out, shape=(H, T), dtype=torch.float32)
+        if not logz.is_contiguous():
+            raise ValueError("logz must be contiguous float32 [H, T]")
+    _require_gpu(v)
+    prm = Params(out, frozen, a.shape[1], softmax_scale, events, kv_heads=0 if Hkv == H else Hkv)
+    prm.p.qk_packed = 1
+    prm.set_strides(v=v, o=out, **({"q": q, "k": k} if n_ord > 0 else {}))
+    prm.p.logz = _ptr(logz)
+    ws_n = workspace_bytes(prm, False)
+    if workspace is not None:
+        _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
+        ws, ws_n = workspace, workspace.numel() * workspace.element_size()
+    else:
+        ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
+    qp, kp = (_ptr(q), _ptr(k)) if n_ord > 0 else (None, None)
+    st = LIB.saf_hybrid_attn_fwd(prm.ref(), qp, kp, _ptr(v), _ptr(a), _ptr(r), _ptr(out),
+                                 _ptr(lse), _ptr(ws), ws_n, _stream_handle(stream))
+    _check(st, "saf_hybrid_attn_fwd")
+    return out, lse
+
+
 def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse=None,
-                        workspace=None, stream=None, events=None, logz=None):
+                        workspace=None, stream=None, events=None, logz=None, qk_packed=False):
     """Forward of the hybrid layer; returns (O, lse).
 
     q: [B, H, T, D]; k, v: [B, Hkv, T, D] with Hkv dividing H (grouped-query
@@ -256,7 +304,11 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     logz: optional fp32 [H, T] precomputed log N of the frozen heads (as
     saf_pattern_lognorm(a, r, T) returns it); the call then skips the
     normaliser computation and copies it into lse.
+    qk_packed: q (and k with multi-head K/V) hold only the ordinary heads in
+    increasing head order ([B, n_ordinary, T, D]); out is [B, H, T, D].
     """
+    if qk_packed:
+        return _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz)
     if not isinstance(k, torch.Tensor) or k.dim() != 4 or q.dim() != 4:
         raise ValueError("q, k and v must be [B, H, T, D] tensors")
     if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
@@ -297,10 +349,23 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
 
 
 def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
-                        dq=None, dk=None, dv=None, workspace=None, stream=None, events=None):
-    """Backward of the hybrid layer; returns (dQ, dK, dV)."""
-    given = {n: t for n, t in dict(dq=dq, dk=dk, dv=dv).items() if t is not None}
-    _check_layer_inputs(v, a, r, q=q, k=k, o=o, dout=dout, **given)
+                        dq=None, dk=None, dv=None, workspace=None, stream=None, events=None,
+                        qk_packed=False):
+    """Backward of the hybrid layer; returns (dQ, dK, dV).  qk_packed: q, k,
+    dq and dk hold only the ordinary heads ([B, n_ordinary, T, D])."""
+    packed = bool(qk_packed)
+    n_ord = _n_ordinary(frozen)
+    if packed:
+        given = {n: t for n, t in dict(dv=dv).items() if t is not None}
+        _check_layer_inputs(v, a, r, o=o, dout=dout, **given)
+        B, H, T, D = v.shape
+        pshape = (B, n_ord, T, D)
+        for name, t in dict(q=q, k=k, dq=dq, dk=dk).items():
+            if t is not None or (name in ("q", "k") and n_ord > 0):
+                _check_like(name, t, v, shape=pshape)
+    else:
+        given = {n: t for n, t in dict(dq=dq, dk=dk, dv=dv).items() if t is not None}
+        _check_layer_inputs(v, a, r, q=q, k=k, o=o, dout=dout, **given)
     B, H, T, D = v.shape
     _check_like("lse", lse, v, shape=(B, H, T), dtype=torch.float32)
     if not lse.is_contiguous():
@@ -308,17 +373,25 @@ def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
     if workspace is not None:
         _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
     _require_gpu(v)
-    mk = lambda: torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)  # noqa: E731
-    dq = mk() if dq is None else dq
-    dk = mk() if dk is None else dk
-    dv = mk() if dv is None else dv
+    hq = n_ord if packed else H
+    mk = lambda n: torch.empty((B, n, T, D), dtype=v.dtype, device=v.device)  # noqa: E731
+    dq = mk(hq) if dq is None else dq
+    dk = mk(hq) if dk is None else dk
+    dv = mk(H) if dv is None else dv
     prm = Params(v, frozen, a.shape[1], softmax_scale, events)
-    prm.set_strides(q=q, k=k, v=v, o=o, do=dout, dq=dq, dk=dk, dv=dv)
+    prm.p.qk_packed = 1 if packed else 0
+    qk = {} if (packed and n_ord == 0) else dict(q=q, k=k, dq=dq, dk=dk)
+    prm.set_strides(v=v, o=o, do=dout, dv=dv, **qk)
+    if packed and n_ord == 0:
+        q = k = None
+        dq_p = dk_p = None
+    else:
+        dq_p, dk_p = dq, dk
     ws_n = workspace_bytes(prm, True)
     if workspace is None:
         workspace = torch.empty(ws_n, dtype=torch.uint8, device=v.device)
     st = LIB.saf_hybrid_attn_bwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                 _ptr(a), _ptr(r), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                 _ptr(a), _ptr(r), _ptr(dq_p), _ptr(dk_p), _ptr(dv), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream_handle(stream))
     _check(st, "saf_hybrid_attn_bwd")
     return dq, dk, dv

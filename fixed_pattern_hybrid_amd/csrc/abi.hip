@@ -42,6 +42,7 @@ int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   if (!supported_d(p->dtype, p->D)) return SAF_EUNSUPPORTED;
   if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return SAF_EINVAL;
   if (!p->frozen) return SAF_EINVAL;
+  if (p->qk_packed != 0 && p->qk_packed != 1) return SAF_EINVAL;
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return SAF_EINVAL;
   int o = 0, f = 0;
   for (int h = 0; h < p->H; ++h) {
@@ -160,6 +161,16 @@ void fill_heads(const saf_attn_params* p, uint8_t* ord, uint8_t* frz, uint8_t* i
   }
 }
 
+// Q/K head slots: h, or the rank among the ordinary heads (packed layout;
+// frozen heads get slot 0, which no kernel uses for them).
+void fill_slots(const saf_attn_params* p, uint8_t* slot) {
+  int o = 0;
+  for (int h = 0; h < p->H; ++h) {
+    slot[h] = (uint8_t)(p->qk_packed ? (p->frozen[h] ? 0 : o) : h);
+    if (!p->frozen[h]) ++o;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -219,6 +230,7 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   args.n_frz = n_frz;
   args.kv_group = p->kv_heads > 0 ? p->H / p->kv_heads : 1;
   fill_heads(p, args.ord_heads, args.frz_heads, nullptr);
+  fill_slots(p, args.qk_slot);
 
   args.logz = p->logz;
 
@@ -291,8 +303,10 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
     if ((st = check_tensor(o, p->o_stride, p)) != SAF_OK) return st;
   }
   if ((st = check_tensor(dout, p->do_stride, p)) != SAF_OK) return st;
-  if ((st = check_tensor(dq, p->dq_stride, p)) != SAF_OK) return st;
-  if ((st = check_tensor(dk, p->dk_stride, p)) != SAF_OK) return st;
+  if (n_ord > 0 || !p->qk_packed) {  // packed with no ordinary head: no dQ/dK rows at all
+    if ((st = check_tensor(dq, p->dq_stride, p)) != SAF_OK) return st;
+    if ((st = check_tensor(dk, p->dk_stride, p)) != SAF_OK) return st;
+  }
   if ((st = check_tensor(dv, p->dv_stride, p)) != SAF_OK) return st;
   if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
   if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
@@ -322,6 +336,8 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   args.n_ord = n_ord;
   args.n_frz = n_frz;
   fill_heads(p, args.ord_heads, args.frz_heads, args.is_frozen);
+  fill_slots(p, args.qk_slot);
+  args.qk_packed = p->qk_packed;
 
   Stages stg{p, stream};
   if (stg.mark() != hipSuccess) return SAF_EHIP;

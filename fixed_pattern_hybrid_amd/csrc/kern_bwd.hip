@@ -90,11 +90,12 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
   const int j = k0 + 32 * w + (l & 31);  // this lane's key
   const int wk_lo = k0 + 32 * w;
 
-  const int64_t qoff = (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
+  const int hs = A.qk_slot[h];  // Q/K/dQ/dK slot of this head
+  const int64_t qoff = (int64_t)b * A.q.sb + (int64_t)hs * A.q.sh;
   const int64_t ooff = (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
   const __bf16* qg = (const __bf16*)A.q.ptr + qoff;
   const __bf16* dog = (const __bf16*)A.dout.ptr + ooff;
-  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)hs * A.k.sh;
   const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
   const float* lse = A.lse + ((int64_t)b * A.H + h) * T;
   const float* dl = A.delta + ((int64_t)b * A.H + h) * T;
@@ -226,7 +227,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
   for (; qt < qt_full; ++qt) tile(qt, std::true_type{});
   for (; qt < nqt; ++qt) tile(qt, std::false_type{});
   store_rows_t<D>(A.dv, b, h, j, T, dva, 1.f);
-  store_rows_t<D>(A.dk, b, h, j, T, dka, A.scale);
+  store_rows_t<D>(A.dk, b, hs, j, T, dka, A.scale);
 }
 
 // ---------------------------------------------------------------------------
@@ -252,7 +253,8 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   const float a2 = (j < T) ? arow[j] * kLog2e : kNegInf;
 
   // frozen heads have no query/key path: dQ and dK rows are exactly +0.0
-  if (j < T && hl == 0) {
+  // (a packed layout has no rows for them)
+  if (j < T && hl == 0 && !A.qk_packed) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
       if (gb < nb) {
@@ -396,9 +398,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   const int i = q0 + 32 * w + (l & 31);
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
-  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
+  const int hs = A.qk_slot[h];  // Q/K/dQ/dK slot of this head
+  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)hs * A.q.sh;
   const __bf16* dog = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh;
-  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)h * A.k.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)hs * A.k.sh;
   const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)h * A.v.sh;
 
   bf16x8 qf[C::NKS], of[C::NKS];
@@ -503,7 +506,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   int t = 0;
   for (; t < t_diag; ++t) tile(t, std::false_type{});
   for (; t < ntiles; ++t) tile(t, std::true_type{});
-  store_rows_t<D>(A.dq, b, h, i, T, dqa, A.scale);
+  store_rows_t<D>(A.dq, b, hs, i, T, dqa, A.scale);
 }
 
 template <typename K>

@@ -50,6 +50,8 @@ __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
   const int bh = blockIdx.y;
   const int b = bh / A.H, h = bh - b * A.H;
   const int hk = h / A.kv_group;  // key/value head of this query head
+  const int hq = A.qk_slot[h];    // its Q slot
+  const int kk = A.kv_group == 1 ? hq : hk;  // its K slot
   const int i = blockIdx.x * kRowsPerBlock + threadIdx.x;
   const int T = A.T;
   if (i >= T) return;
@@ -74,12 +76,12 @@ __global__ __launch_bounds__(kRowsPerBlock) void fwd_f32(FwdArgs A) {
     return;
   }
   float q[D];
-  load_row<D>(q, rowp(A.q, b, h, i));
+  load_row<D>(q, rowp(A.q, b, hq, i));
   float m = kNegInf;
-  for (int j = 0; j <= i; ++j) m = fmaxf(m, dot_row<D>(q, rowp(A.k, b, hk, j)) * A.scale_log2);
+  for (int j = 0; j <= i; ++j) m = fmaxf(m, dot_row<D>(q, rowp(A.k, b, kk, j)) * A.scale_log2);
   float lsum = 0.f;
   for (int j = 0; j <= i; ++j) {
-    const float p = fast_exp2(dot_row<D>(q, rowp(A.k, b, hk, j)) * A.scale_log2 - m);
+    const float p = fast_exp2(dot_row<D>(q, rowp(A.k, b, kk, j)) * A.scale_log2 - m);
     lsum += p;
     const float* vr = rowp(A.v, b, hk, j);
 #pragma unroll
@@ -98,6 +100,7 @@ __global__ __launch_bounds__(kRowsPerBlock) void bwd_pre_f32(BwdArgs A) {
   const int i = blockIdx.x * kRowsPerBlock + threadIdx.x;
   if (i >= A.T) return;
   if (A.is_frozen[h]) {
+    if (A.qk_packed) return;  // no dQ/dK rows for frozen heads
     float* dq = rowp_w(A.dq, b, h, i);
     float* dk = rowp_w(A.dk, b, h, i);
 #pragma unroll
@@ -142,12 +145,13 @@ __global__ __launch_bounds__(kRowsPerBlock) void bwd_kv_f32(BwdArgs A) {
   }
   const float* dl = A.delta + ((int64_t)b * A.H + h) * T;
   float k[D], v[D], dk[D];
-  load_row<D>(k, rowp(A.k, b, h, j));
+  const int hs = A.qk_slot[h];  // Q/K/dQ/dK slot of this head
+  load_row<D>(k, rowp(A.k, b, hs, j));
   load_row<D>(v, rowp(A.v, b, h, j));
 #pragma unroll
   for (int d = 0; d < D; ++d) dk[d] = 0.f;
   for (int i = j; i < T; ++i) {
-    const float* qr = rowp(A.q, b, h, i);
+    const float* qr = rowp(A.q, b, hs, i);
     const float* g = rowp(A.dout, b, h, i);
     const float p = fast_exp2(dot_row<D>(k, qr) * A.scale_log2 - lse[i] * kLog2e);
     const float dp = dot_row<D>(v, g);
@@ -158,7 +162,7 @@ __global__ __launch_bounds__(kRowsPerBlock) void bwd_kv_f32(BwdArgs A) {
       dk[d] = fmaf(ds, qr[d], dk[d]);
     }
   }
-  float* dkrow = rowp_w(A.dk, b, h, j);
+  float* dkrow = rowp_w(A.dk, b, hs, j);
 #pragma unroll
   for (int d = 0; d < D; ++d) {
     dvrow[d] = dv[d];
@@ -177,18 +181,19 @@ __global__ __launch_bounds__(kRowsPerBlock) void bwd_q_f32(BwdArgs A) {
   const float l2 = A.lse[rv] * kLog2e;
   const float dl = A.delta[rv];
   float q[D], g[D], dq[D];
-  load_row<D>(q, rowp(A.q, b, h, i));
+  const int hs = A.qk_slot[h];  // Q/K/dQ/dK slot of this head
+  load_row<D>(q, rowp(A.q, b, hs, i));
   load_row<D>(g, rowp(A.dout, b, h, i));
 #pragma unroll
   for (int d = 0; d < D; ++d) dq[d] = 0.f;
   for (int j = 0; j <= i; ++j) {
-    const float* kr = rowp(A.k, b, h, j);
+    const float* kr = rowp(A.k, b, hs, j);
     const float p = fast_exp2(dot_row<D>(q, kr) * A.scale_log2 - l2);
     const float ds = p * (dot_row<D>(g, rowp(A.v, b, h, j)) - dl);
 #pragma unroll
     for (int d = 0; d < D; ++d) dq[d] = fmaf(ds, kr[d], dq[d]);
   }
-  float* out = rowp_w(A.dq, b, h, i);
+  float* out = rowp_w(A.dq, b, hs, i);
 #pragma unroll
   for (int d = 0; d < D; ++d) out[d] = dq[d] * A.scale;
 }

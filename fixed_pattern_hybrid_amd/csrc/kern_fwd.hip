@@ -87,8 +87,9 @@ __device__ __forceinline__ void fwd_ordinary(const FwdArgs& A, int b, int h, int
   const int wq_lo = q0 + 32 * w, wq_hi = wq_lo + 31;
 
   const int hk = h / A.kv_group;  // key/value head of this query head
-  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)h * A.q.sh;
-  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)hk * A.k.sh;
+  const int kslot = A.kv_group == 1 ? A.qk_slot[h] : hk;  // its K slot
+  const __bf16* qg = (const __bf16*)A.q.ptr + (int64_t)b * A.q.sb + (int64_t)A.qk_slot[h] * A.q.sh;
+  const __bf16* kg = (const __bf16*)A.k.ptr + (int64_t)b * A.k.sb + (int64_t)kslot * A.k.sh;
   const __bf16* vg = (const __bf16*)A.v.ptr + (int64_t)b * A.v.sb + (int64_t)hk * A.v.sh;
 
   // Q as the B operand of S^T = K Q^T: lane holds Q[i][16ks + 8*hl + 0..7].

@@ -52,6 +52,9 @@ struct FwdArgs {
   const float* logz;
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
+  // head slot of head h in Q (and K with multi-head K/V): h, or h's rank
+  // among the ordinary heads when the caller packs Q/K without frozen slots
+  uint8_t qk_slot[kMaxHeads];
 };
 
 // Backward arguments (both dtypes).
@@ -70,6 +73,10 @@ struct BwdArgs {
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
   uint8_t is_frozen[kMaxHeads];
+  // head slot of head h in Q, K, dQ and dK (as in FwdArgs); qk_packed: the
+  // frozen heads have no slot there (their zero dQ/dK rows are not written)
+  uint8_t qk_slot[kMaxHeads];
+  int qk_packed;
 };
 
 // Pattern-parameter gradients of frozen heads (both dtypes).

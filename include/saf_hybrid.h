@@ -125,6 +125,16 @@ typedef struct saf_attn_params {
    * a and r passed, which the library does not check.  NULL: computed by the
    * call.  Read by saf_hybrid_attn_fwd only. */
   const float* logz;
+  /* Q/K layout (the pages give replaced heads no query or key slot, Section
+   * 3.3 and Appendix D.2).  0: q, k, dq and dk have all H heads; frozen
+   * heads' q, k are not read and their dq, dk slices are written +0.0.
+   * 1 (packed): q and dq hold only the ordinary heads, in increasing head
+   * order (slot s = the s-th ordinary head); so do k and dk with multi-head
+   * K/V, while with kv_heads < H, k keeps its kv_heads key/value heads.
+   * Nothing is read or written for frozen heads there (with no ordinary
+   * head, q, k, dq and dk may be NULL).  v, o, dO and dV always have all
+   * heads.  Strides of the packed tensors step over their own heads. */
+  int32_t qk_packed;
 } saf_attn_params;
 
 /*
@@ -154,7 +164,8 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k,
 /*
  * Backward pass of the hybrid layer (Section 3.3; Appendix D.2 key-block and
  * query-block passes).  Given dO and the forward's o and lse, writes
- *   dq, dk : ordinary heads' gradients; frozen heads' slices := +0.0;
+ *   dq, dk : ordinary heads' gradients; frozen heads' slices := +0.0
+ *            (packed layout, p->qk_packed: no slices for frozen heads);
  *   dv     : gradients of every head (frozen: W^T dO).
  * q, k of frozen heads are not read.  o is read for ordinary heads only.
  * ws: at least saf_hybrid_attn_workspace_bytes(p, 1) bytes, 256-byte aligned.

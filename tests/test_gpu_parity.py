@@ -529,3 +529,49 @@ def test_frozen_wide_range_patterns(B, spike):
         e = rel_l2(host(dv[:, h]), ref_dv[:, h])
         say(f"  h{h} dV rel-L2 {e:.3e}")
         assert e <= BF16_GRAD_RELL2
+
+
+# ---------------------------------------------------------------------------
+# Packed Q/K layout: replaced heads have no query or key slot (Section 3.3,
+# Appendix D.2).  The same kernels run with a head-to-slot map, so the
+# results must equal the full layout's bit for bit.
+# ---------------------------------------------------------------------------
+
+
+def _packed_vs_full(B, cfg):
+    inp = make_inputs(cfg, with_do=cfg.bwd)
+    dev = upload(inp)
+    fz = [int(x) for x in inp.frozen]
+    ordh = [h for h in range(cfg.H) if not fz[h]]
+    gqa = cfg.kv_heads not in (0, None, cfg.H)
+    qp = dev["q"][:, ordh].contiguous() if ordh else None
+    kp = (dev["k"] if gqa else dev["k"][:, ordh].contiguous()) if ordh else None
+    say(f"packed Q/K: {cfg.name} frozen={tuple(h for h in range(cfg.H) if fz[h])}")
+    O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    Op, Lp = B.saf_hybrid_attn_fwd(qp, kp, dev["v"], fz, dev["a"], dev["r"], qk_packed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(O, Op) and torch.equal(L, Lp)
+    if not cfg.bwd:
+        return
+    dq, dk, dv = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"])
+    dqp, dkp, dvp = B.saf_hybrid_attn_bwd(qp, kp, dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"],
+                                          qk_packed=True)
+    torch.cuda.synchronize()
+    assert tuple(dqp.shape) == (cfg.B, len(ordh), cfg.T, cfg.D)
+    assert torch.equal(dv, dvp)
+    if ordh:
+        assert torch.equal(dq[:, ordh], dqp) and torch.equal(dk[:, ordh], dkp)
+
+
+@pytest.mark.parametrize("key,frozen", [("pages_check_t129", (3,)), ("pages_check_t129", (0, 2)),
+                                        ("pages_check_t129", (0, 1, 2, 3)), ("pages_check_t129", ()),
+                                        ("tiny", (1,)), ("tiny", (0, 1, 2, 3))])
+def test_packed_qk_layout_matches_full(B, key, frozen):
+    cfg = CONFIGS[key].with_(frozen=frozen, name=f"{key}_packed{len(frozen)}")
+    _packed_vs_full(B, cfg)
+
+
+def test_packed_q_grouped_query_forward(B):
+    cfg = CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, B=2, T=200, prior_len=None, frozen=(1, 4, 5),
+                                            bwd=False, name="gqa_packed_q")
+    _packed_vs_full(B, cfg)
