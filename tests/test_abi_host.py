@@ -96,6 +96,8 @@ FAKE = 0x10000  # a 16-byte aligned non-null address; never dereferenced on thes
         ({"kv_heads": -1}, -1),
         ({"kv_heads": 8}, -1),
         ({"softmax_scale": float("nan")}, -1),
+        ({"qk_packed": 2}, -1),
+        ({"qk_packed": -1}, -1),
     ],
 )
 def test_fwd_rejects_bad_params(b, mut, expect):
