@@ -262,8 +262,10 @@ def _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, strea
         raise ValueError(f"v has {Hkv} heads, which must divide the {H} heads of the frozen mask")
     if out is None:
         out = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
+    # B, T and D of the call come from v: a caller's out must have exactly
+    # v's batch, length and head dimension with all H heads
+    _check_like("out", out, v, shape=(B, H, T, D))
     _check_layer_inputs(out, a, r)
-    _check_like("v", v, out, shape=(B, Hkv, T, D))
     if n_ord > 0:
         _check_like("q", q, out, shape=(B, n_ord, T, D))
         _check_like("k", k, out, shape=(B, n_ord if Hkv == H else Hkv, T, D))

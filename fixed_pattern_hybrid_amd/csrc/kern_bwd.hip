@@ -1,8 +1,9 @@
 // Backward of the SAF hybrid attention layer, bf16, gfx950
 // ("When Can Attention Heads Be Statically Defined?", Section 3.3 and
-// Appendix D.2: key-block programs accumulate value gradients for every head
-// and key gradients for ordinary heads; a separate query-block pass computes
-// query gradients of ordinary heads; frozen heads get dV = W^T dO only).
+// Appendix D.2).  Two launches: the first walks the key tiles of each
+// ordinary query block and writes dQ (plus delta); the second walks the query
+// tiles of each 128-key block and writes dV of every head and dK of the
+// ordinary heads.  A frozen head contributes only dV = W^T dO.
 //
 // Ordinary heads follow the chain rule of causal softmax attention
 // (Appendix A.1, Equations 5-7) with P recomputed from the saved row

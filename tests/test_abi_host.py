@@ -230,6 +230,44 @@ def test_binding_rejects_mismatched_tensors(b):
         b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r)
 
 
+def test_binding_packed_layout_rejects_mismatched_tensors(b):
+    # Packed Q/K layout: B, T and D come from v, so a caller's out, q or k
+    # of another shape must be refused before the library is called.
+    import torch
+
+    B_, H, T, D = 1, 4, 64, 64
+    fz = [0, 1, 0, 1]
+    n_ord = 2
+    mk = lambda *s, dt=torch.bfloat16: torch.zeros(*s, dtype=dt)  # noqa: E731
+    q, k = mk(B_, n_ord, T, D), mk(B_, n_ord, T, D)
+    v = mk(B_, H, T, D)
+    a, r = mk(H, T, dt=torch.float32), mk(H, T, dt=torch.float32)
+    # an out longer than v (the case that would read q/k/v and write lse
+    # past their ends)
+    with pytest.raises(ValueError, match="out has shape"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=mk(B_, H, 4 * T, D), qk_packed=True)
+    with pytest.raises(ValueError, match="out has shape"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=mk(B_ + 1, H, T, D), qk_packed=True)
+    with pytest.raises(ValueError, match="out has dtype"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=mk(B_, H, T, D, dt=torch.float32), qk_packed=True)
+    with pytest.raises(ValueError, match="q has shape"):
+        b.saf_hybrid_attn_fwd(mk(B_, H, T, D), k, v, fz, a, r, qk_packed=True)
+    with pytest.raises(ValueError, match="k has shape"):
+        b.saf_hybrid_attn_fwd(q, mk(B_, n_ord, T + 1, D), v, fz, a, r, qk_packed=True)
+    lse = mk(B_, H, T, dt=torch.float32)
+    with pytest.raises(ValueError, match="q has shape"):
+        b.saf_hybrid_attn_bwd(mk(B_, H, T, D), k, v, v, v, lse, fz, a, r, qk_packed=True)
+    with pytest.raises(ValueError, match="dq has shape"):
+        b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r, dq=mk(B_, n_ord, T // 2, D), qk_packed=True)
+    with pytest.raises(ValueError, match="shape"):
+        b.saf_hybrid_attn_bwd(q, k, v, mk(B_, H, 2 * T, D), v, lse, fz, a, r, qk_packed=True)
+    # consistent host tensors pass every shape check and stop at the device check
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_hybrid_attn_fwd(q, k, v, fz, a, r, out=mk(B_, H, T, D), qk_packed=True)
+    with pytest.raises(ValueError, match="GPU"):
+        b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r, qk_packed=True)
+
+
 def test_pattern_grad_workspace_and_rejects(b):
     # bf16: D_b of frozen rows, then per program (frozen head, batch group of
     # 2, key block of 128, query chunk of 512) 128 column and 640 diagonal

@@ -52,6 +52,13 @@ def test_flop_accounting_per_pair():
     assert f["total"] == 4 * cfg.D * P
 
 
+def test_calibration_flop_accounting():
+    # shifted-sum update per entry: log2 A (FMA), A log2 A (FMA), A - A0,
+    # s1 += d, s2 += d*d (FMA): 2 + 2 + 1 + 1 + 2 flops, the exponential not
+    # counted
+    assert bench.CALIB_FLOPS_PER_UPDATE == 8
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)

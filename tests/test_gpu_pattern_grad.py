@@ -33,6 +33,8 @@ import torch
 import oracle
 from synth import CONFIGS, make_inputs
 from _helpers import BF16_GRAD_RELL2, host, rel_l2, say, upload
+from _helpers import forward_rounding_sigma as _forward_rounding_sigma
+from _helpers import half_ulp as _half_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -60,33 +62,6 @@ def _fwd_then_pgrad(B, inp, dev, strided=False, sentinel=7.0):
     B.saf_pattern_grad(v, O, do, L, fz, dev["a"], dev["r"], da=da, dr=dr)
     torch.cuda.synchronize()
     return host(da), host(dr), fz
-
-
-def _half_ulp(x, bits):
-    ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)
-    return 0.5 * 2.0 ** (np.floor(np.log2(ax)) - (bits - 1))
-
-
-def _forward_rounding_sigma(cfg, inp, h):
-    """L2 norms over the entries of the standard deviations of da and dr of
-    head h caused by the forward's rounding inside D (module docstring)."""
-    bits = 8 if cfg.dtype == "bf16" else 24  # significand bits of the storage type
-    T = cfg.T
-    P = oracle.frozen_pattern(inp.a[h], inp.r[h], T)
-    va = np.zeros(T)
-    vr = np.zeros(T)
-    for b in range(cfg.B):
-        v = np.asarray(inp.v[b, h], np.float64)
-        do = np.asarray(inp.do[b, h], np.float64)
-        O = P @ v
-        var_d = (do ** 2 * _half_ulp(O, bits) ** 2 / 3).sum(axis=1)
-        if cfg.dtype == "bf16":
-            var_d += (np.where(P > 0, _half_ulp(P, bits), 0.0) ** 2 / 3 * (do @ v.T) ** 2).sum(axis=1)
-        Wv = P ** 2 * var_d[:, None]
-        va += Wv.sum(axis=0)
-        for i in range(T):
-            vr[: i + 1] += Wv[i, i::-1]
-    return float(np.sqrt(va.sum())), float(np.sqrt(vr.sum()))
 
 
 def run_pgrad_parity(B, cfg, strided=False):
