@@ -22,11 +22,14 @@ SAF_EINVAL = -1
 SAF_EUNSUPPORTED = -2
 SAF_EWORKSPACE = -3
 SAF_EHIP = -4
+SAF_ESCRATCH = -5
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SAF_F32 = 0
 SAF_BF16 = 1
 
 EXPORTED = (
     "saf_hybrid_attn_fwd",
+    "saf_hybrid_attn_fwd_noalloc",
     "saf_hybrid_attn_bwd",
     "saf_hybrid_attn_workspace_bytes",
     "saf_pattern_dense",
@@ -92,6 +95,8 @@ def _load():
     pp = ctypes.POINTER(SafParams)
     lib.saf_hybrid_attn_fwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.saf_hybrid_attn_fwd.restype = ctypes.c_int
+    lib.saf_hybrid_attn_fwd_noalloc.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.saf_hybrid_attn_fwd_noalloc.restype = ctypes.c_int
     lib.saf_hybrid_attn_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.saf_hybrid_attn_bwd.restype = ctypes.c_int
     lib.saf_hybrid_attn_workspace_bytes.argtypes = [pp, ctypes.c_int]
@@ -251,7 +256,19 @@ def _n_ordinary(frozen) -> int:
     return len(frozen) - sum(int(x) for x in frozen)
 
 
-def _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz):
+def _fwd_call(prm, q, k, v, a, r, out, lse, ws, ws_n, stream, noalloc):
+    if noalloc:
+        st = LIB.saf_hybrid_attn_fwd_noalloc(prm.ref(), q, k, _ptr(v), _ptr(a), _ptr(r), _ptr(out),
+                                             _ptr(lse), _stream_handle(stream))
+        _check(st, "saf_hybrid_attn_fwd_noalloc")
+    else:
+        st = LIB.saf_hybrid_attn_fwd(prm.ref(), q, k, _ptr(v), _ptr(a), _ptr(r), _ptr(out), _ptr(lse),
+                                     _ptr(ws), ws_n, _stream_handle(stream))
+        _check(st, "saf_hybrid_attn_fwd")
+
+
+def _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz,
+                noalloc=False):
     """saf_hybrid_attn_fwd with q (and k, for multi-head K/V) holding only
     the ordinary heads, in increasing head order."""
     if not isinstance(v, torch.Tensor) or v.dim() != 4:
@@ -283,21 +300,23 @@ def _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, strea
     prm.p.qk_packed = 1
     prm.set_strides(v=v, o=out, **({"q": q, "k": k} if n_ord > 0 else {}))
     prm.p.logz = _ptr(logz)
-    ws_n = workspace_bytes(prm, False)
-    if workspace is not None:
+    ws, ws_n = None, 0
+    if noalloc:
+        pass
+    elif workspace is not None:
         _check_like("workspace", workspace, v, shape=workspace.shape, dtype=workspace.dtype)
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
+        ws_n = workspace_bytes(prm, False)
         ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
     qp, kp = (_ptr(q), _ptr(k)) if n_ord > 0 else (None, None)
-    st = LIB.saf_hybrid_attn_fwd(prm.ref(), qp, kp, _ptr(v), _ptr(a), _ptr(r), _ptr(out),
-                                 _ptr(lse), _ptr(ws), ws_n, _stream_handle(stream))
-    _check(st, "saf_hybrid_attn_fwd")
+    _fwd_call(prm, qp, kp, v, a, r, out, lse, ws, ws_n, stream, noalloc)
     return out, lse
 
 
 def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse=None,
-                        workspace=None, stream=None, events=None, logz=None, qk_packed=False):
+                        workspace=None, stream=None, events=None, logz=None, qk_packed=False,
+                        _noalloc=False):
     """Forward of the hybrid layer; returns (O, lse).
 
     q: [B, H, T, D]; k, v: [B, Hkv, T, D] with Hkv dividing H (grouped-query
@@ -310,7 +329,8 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     increasing head order ([B, n_ordinary, T, D]); out is [B, H, T, D].
     """
     if qk_packed:
-        return _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz)
+        return _fwd_packed(q, k, v, frozen, a, r, softmax_scale, out, lse, workspace, stream, events, logz,
+                           _noalloc)
     if not isinstance(k, torch.Tensor) or k.dim() != 4 or q.dim() != 4:
         raise ValueError("q, k and v must be [B, H, T, D] tensors")
     if k.shape[0] != q.shape[0] or k.shape[2:] != q.shape[2:]:
@@ -339,15 +359,29 @@ def saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=None, out=None, lse
     prm = Params(q, frozen, a.shape[1], softmax_scale, events, kv_heads=0 if Hk == H else Hk)
     prm.set_strides(q=q, k=k, v=v, o=out)
     prm.p.logz = _ptr(logz)
-    ws_n = workspace_bytes(prm, False)
-    if workspace is not None:
+    ws, ws_n = None, 0
+    if _noalloc:
+        pass
+    elif workspace is not None:
         ws, ws_n = workspace, workspace.numel() * workspace.element_size()
     else:
+        ws_n = workspace_bytes(prm, False)
         ws = torch.empty(ws_n, dtype=torch.uint8, device=v.device) if ws_n else None
-    st = LIB.saf_hybrid_attn_fwd(prm.ref(), _ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(r), _ptr(out),
-                                 _ptr(lse), _ptr(ws), ws_n, _stream_handle(stream))
-    _check(st, "saf_hybrid_attn_fwd")
+    _fwd_call(prm, _ptr(q), _ptr(k), v, a, r, out, lse, ws, ws_n, stream, _noalloc)
     return out, lse
+
+
+def saf_hybrid_attn_fwd_noalloc(q, k, v, frozen, a, r, out, lse, softmax_scale=None, stream=None,
+                                events=None, logz=None, qk_packed=False):
+    """saf_hybrid_attn_fwd without a workspace (the library's static scratch
+    of the current device; for callers that cannot allocate).  The caller
+    passes the outputs out ([B, H, T, D]) and lse (fp32 [B, H, T]); nothing
+    is allocated.  Shapes needing more than NOALLOC_SCRATCH_BYTES of scratch
+    raise SafError (SAF_ESCRATCH).  Calls overlapping on one GPU race."""
+    if out is None or lse is None:
+        raise ValueError("saf_hybrid_attn_fwd_noalloc needs caller-provided out and lse")
+    return saf_hybrid_attn_fwd(q, k, v, frozen, a, r, softmax_scale=softmax_scale, out=out, lse=lse,
+                               stream=stream, events=events, logz=logz, qk_packed=qk_packed, _noalloc=True)
 
 
 def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <climits>
 #include <cstring>
+#include <mutex>
 
 namespace {
 
@@ -171,32 +172,10 @@ void fill_slots(const saf_attn_params* p, uint8_t* slot) {
   }
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* saf_status_string(int status) {
-  switch (status) {
-    case SAF_OK: return "ok";
-    case SAF_EINVAL: return "invalid argument (pointer, size, stride or alignment)";
-    case SAF_EUNSUPPORTED: return "unsupported configuration (head dim, dtype or size)";
-    case SAF_EWORKSPACE: return "workspace missing, misaligned or too small";
-    case SAF_EHIP: return "HIP runtime or launch failure";
-    default: return "unknown status";
-  }
-}
-
-int32_t saf_version(void) { return kVersion; }
-
-size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd) {
-  int o, f;
-  if (check_params(p, &o, &f) != SAF_OK) return 0;
-  return for_bwd ? bwd_ws_bytes(p) : fwd_ws_bytes(p, f);
-}
-
-int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
-                        const float* a, const float* r, void* o, float* lse, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+// Argument checks of the forward (everything but the workspace); counts
+// the heads of each kind.
+int fwd_check(const saf_attn_params* p, const void* q, const void* k, const void* v, const float* a,
+              const float* r, const void* o, const float* lse, int* n_ord_out, int* n_frz_out) {
   int n_ord = 0, n_frz = 0;
   int st = check_params(p, &n_ord, &n_frz);
   if (st != SAF_OK) return st;
@@ -209,9 +188,15 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
   if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
   if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
   if (p->logz && !aligned(p->logz, 4)) return SAF_EINVAL;
-  const size_t need = fwd_ws_bytes(p, n_frz);
-  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return SAF_EWORKSPACE;
+  *n_ord_out = n_ord;
+  *n_frz_out = n_frz;
+  return SAF_OK;
+}
 
+// The forward's kernels on `stream`, after fwd_check; ws holds at least
+// fwd_ws_bytes(p, n_frz) bytes, 256-byte aligned.
+int fwd_run(const saf_attn_params* p, int n_ord, int n_frz, const void* q, const void* k, const void* v,
+            const float* a, const float* r, void* o, float* lse, void* ws, hipStream_t stream) {
   FwdArgs args;
   std::memset(&args, 0, sizeof(args));
   args.q = ref(q, p->q_stride);
@@ -286,6 +271,76 @@ int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, 
     if (stg.mark() != hipSuccess) return SAF_EHIP;
   }
   return SAF_OK;
+}
+
+// Scratch of saf_hybrid_attn_fwd_noalloc: one array per device, for callers
+// that cannot allocate.  Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, taken once per
+// device with that device current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[SAF_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch, or null on a HIP error.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* saf_status_string(int status) {
+  switch (status) {
+    case SAF_OK: return "ok";
+    case SAF_EINVAL: return "invalid argument (pointer, size, stride or alignment)";
+    case SAF_EUNSUPPORTED: return "unsupported configuration (head dim, dtype or size)";
+    case SAF_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case SAF_EHIP: return "HIP runtime or launch failure";
+    case SAF_ESCRATCH: return "shape needs more scratch than the no-allocation entry point holds";
+    default: return "unknown status";
+  }
+}
+
+int32_t saf_version(void) { return kVersion; }
+
+size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd) {
+  int o, f;
+  if (check_params(p, &o, &f) != SAF_OK) return 0;
+  return for_bwd ? bwd_ws_bytes(p) : fwd_ws_bytes(p, f);
+}
+
+int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
+                        const float* a, const float* r, void* o, float* lse, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  int n_ord = 0, n_frz = 0;
+  int st = fwd_check(p, q, k, v, a, r, o, lse, &n_ord, &n_frz);
+  if (st != SAF_OK) return st;
+  const size_t need = fwd_ws_bytes(p, n_frz);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256))) return SAF_EWORKSPACE;
+  return fwd_run(p, n_ord, n_frz, q, k, v, a, r, o, lse, ws, stream);
+}
+
+int saf_hybrid_attn_fwd_noalloc(const saf_attn_params* p, const void* q, const void* k, const void* v,
+                                const float* a, const float* r, void* o, float* lse,
+                                hipStream_t stream) {
+  int n_ord = 0, n_frz = 0;
+  int st = fwd_check(p, q, k, v, a, r, o, lse, &n_ord, &n_frz);
+  if (st != SAF_OK) return st;
+  if (fwd_ws_bytes(p, n_frz) > SAF_NOALLOC_SCRATCH_BYTES) return SAF_ESCRATCH;
+  void* ws = nullptr;
+  if (fwd_ws_bytes(p, n_frz) > 0 && !(ws = scratch_ptr())) return SAF_EHIP;
+  return fwd_run(p, n_ord, n_frz, q, k, v, a, r, o, lse, ws, stream);
 }
 
 int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, const void* v,

@@ -72,6 +72,8 @@ extern "C" {
 #define SAF_EUNSUPPORTED (-2) /* valid but not implemented: D, dtype, H */
 #define SAF_EWORKSPACE (-3)   /* workspace missing or too small */
 #define SAF_EHIP (-4)         /* a HIP launch or runtime call failed */
+#define SAF_ESCRATCH (-5)     /* saf_hybrid_attn_fwd_noalloc: the shape needs more
+                                 than SAF_NOALLOC_SCRATCH_BYTES of scratch */
 
 /* Element types of Q, K, V, O, dO, dQ, dK, dV. */
 #define SAF_F32 0
@@ -81,6 +83,8 @@ extern "C" {
 #define SAF_MAX_HEADS 256
 #define SAF_MAX_T (1 << 20)
 #define SAF_MAX_T_STRIDE (1 << 24) /* elements between consecutive rows */
+/* Scratch each GPU holds for saf_hybrid_attn_fwd_noalloc (32 MiB). */
+#define SAF_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 /* Also rejected with SAF_EUNSUPPORTED: B * H * T > 2^40; for bf16,
  * B * H * ceil(T / 128) > 2^31 - 1 (programs per launch); for fp32,
  * B * H > 65535. */
@@ -160,6 +164,31 @@ typedef struct saf_attn_params {
 int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k,
                         const void* v, const float* a, const float* r, void* o,
                         float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * saf_hybrid_attn_fwd for callers that cannot allocate device memory or pass
+ * a workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, layout, semantics and results as
+ * saf_hybrid_attn_fwd (the same kernels; bitwise the same outputs), minus the
+ * workspace: the normaliser partials live in a static scratch array of
+ * SAF_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends.  The call allocates nothing and issues no memset.
+ *   - A shape whose forward needs more scratch than that (bf16 with frozen
+ *     heads: about n_frozen * 32 * T * 8 bytes at most, see ws above; e.g.
+ *     3 frozen heads at T = 32768 need 25.2 MB) is rejected with
+ *     SAF_ESCRATCH before anything is enqueued.  fp32, no frozen head or a
+ *     given p->logz need no scratch.
+ *   - The scratch of the CURRENT device is used; `stream` must belong to it.
+ *     The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress); make it outside stream capture.
+ *   - Every call on a GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs to start at zero): calls that
+ *     overlap in time on one GPU (other streams, other host threads) race
+ *     and must be serialised by the caller.
+ */
+int saf_hybrid_attn_fwd_noalloc(const saf_attn_params* p, const void* q, const void* k,
+                                const void* v, const float* a, const float* r, void* o,
+                                float* lse, hipStream_t stream);
 
 /*
  * Backward pass of the hybrid layer (Section 3.3; Appendix D.2 key-block and

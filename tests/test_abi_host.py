@@ -268,6 +268,35 @@ def test_binding_packed_layout_rejects_mismatched_tensors(b):
         b.saf_hybrid_attn_bwd(q, k, v, v, v, lse, fz, a, r, qk_packed=True)
 
 
+def test_noalloc_forward_rejects_before_any_hip_call(b):
+    # The no-allocation forward validates like the workspace forward and
+    # refuses shapes whose normaliser partials exceed its static scratch,
+    # all before touching the GPU (here there is none).
+    import ctypes
+
+    assert b.NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert "scratch" in b.status_string(b.SAF_ESCRATCH)
+    FAKE = 1 << 20  # 16-byte aligned, never dereferenced on these paths
+    T = 1 << 17
+    fz = (ctypes.c_uint8 * 4)(0, 1, 1, 0)
+    p = b.SafParams()
+    p.struct_bytes = ctypes.sizeof(b.SafParams)
+    p.B, p.H, p.T, p.D, p.prior_len, p.dtype = 1, 4, T, 64, T, b.SAF_BF16
+    p.frozen = ctypes.cast(fz, ctypes.POINTER(ctypes.c_uint8))
+    for name in ("q", "k", "v", "o"):
+        setattr(p, name + "_stride", b._i64x3(4 * T * 64, T * 64, 64))
+    need = b.LIB.saf_hybrid_attn_workspace_bytes(ctypes.byref(p), 0)
+    assert need > b.NOALLOC_SCRATCH_BYTES  # 2 frozen heads x 32 groups x 2^17 rows x 8 B
+    args = [FAKE] * 7
+    assert b.LIB.saf_hybrid_attn_fwd_noalloc(ctypes.byref(p), *args, None) == b.SAF_ESCRATCH
+    # argument errors come first, as in the workspace forward
+    bad = list(args)
+    bad[6] = FAKE + 2  # misaligned lse
+    assert b.LIB.saf_hybrid_attn_fwd_noalloc(ctypes.byref(p), *bad, None) == b.SAF_EINVAL
+    p.D = 80
+    assert b.LIB.saf_hybrid_attn_fwd_noalloc(ctypes.byref(p), *args, None) == b.SAF_EUNSUPPORTED
+
+
 def test_pattern_grad_workspace_and_rejects(b):
     # bf16: D_b of frozen rows, then per program (frozen head, batch group of
     # 2, key block of 128, query chunk of 512) 128 column and 640 diagonal
