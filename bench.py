@@ -446,6 +446,57 @@ PAGES_UPDATE_SPEEDUPS = [
 ]
 
 
+def fused_dq_leg(B, cfg, q, k, v, do, a, r, fz, o, lse, stream, two_pass_ms, reps: int = 20):
+    """The backward's other schedule, fused dQ (one key-block pass that also
+    adds each program's dQ into an fp32 accumulator with atomic adds, no
+    query-block pass), timed at the same shape with its kernels bracketed by
+    the library's stage events.  Not part of the headline step, whose
+    backward is the deterministic two-pass schedule."""
+    import numpy as np
+    import torch
+
+    g = [torch.empty_like(v) for _ in range(3)]
+    prm = B.Params(v, fz, a.shape[1])
+    prm.p.fused_dq = 1
+    ws = torch.empty(max(B.workspace_bytes(prm, True), 256), dtype=torch.uint8, device=v.device)
+    has_ord = not all(fz)
+    names = ["bwd_pre", "bwd_kvq", "dq_convert"] if has_ord else ["bwd_kvq"]
+
+    def call(evs=None):
+        B.saf_hybrid_attn_bwd(q, k, v, o, do, lse, fz, a, r, dq=g[0], dk=g[1], dv=g[2], workspace=ws,
+                              stream=stream, events=evs, fused_dq=True)
+
+    for _ in range(3):
+        call()
+    evs = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        for x in e:
+            x.record(stream)
+        evs.append(e)
+    torch.cuda.synchronize()
+    for s_ in range(reps):
+        call(evs[s_])
+    torch.cuda.synchronize()
+    kms = {n: float(np.mean([evs[s_][x].elapsed_time(evs[s_][x + 1]) for s_ in range(reps)]))
+           for x, n in enumerate(names)}
+    tot = float(np.mean([evs[s_][0].elapsed_time(evs[s_][-1]) for s_ in range(reps)]))
+    return {"bwd_ms": round(tot, 4), "kernel_ms": {n: round(x, 4) for n, x in kms.items()},
+            "two_pass_bwd_ms": round(two_pass_ms, 4), "fused_over_two_pass": round(tot / two_pass_ms, 3),
+            "atomic_bytes": pairs_tiles_bytes(cfg),
+            "note": "fused-dQ backward schedule (fused_dq = 1): dQ accumulated with fp32 atomic adds inside the "
+                    "key-block pass; the headline uses the two-pass schedule"}
+
+
+def pairs_tiles_bytes(cfg):
+    """fp32 bytes the fused schedule adds atomically: one 64-query x D block
+    per (ordinary (b, h), 128-key block, 64-query tile at or after it)."""
+    nkb = (cfg.T + 127) // 128
+    nqt = (cfg.T + 63) // 64
+    tiles = sum(nqt - 2 * kb for kb in range(nkb))
+    return cfg.B * (cfg.H - len(cfg.frozen)) * tiles * 64 * cfg.D * 4
+
+
 def layer_vs_all_ordinary(B, cfg, q, k, v, do, a, r, fz, reps: int = 10):
     """fwd+bwd of the layer with every head ordinary over the same call with
     the workload's frozen heads (same inputs and shape), 8 samples of `reps`
@@ -712,6 +763,8 @@ def main():
         tp = trainable_pattern_leg(B, cfg, dict(v=v, o=o, do=do, lse=lse, a=a, r=r, fz=fz), stream)
         tp["over_layer_step"] = round(tp["ms"] / ms, 4)
         out["trainable_pattern"] = tp
+    if do is not None and cfg.dtype == "bf16" and D == 64 and has_ord:
+        out["bwd_fused_dq"] = fused_dq_leg(B, cfg, q, k, v, do, a, r, fz, o, lse, stream, out["bwd_ms"])
     if not args.no_per_head and do is not None:
         out["per_head"] = per_head_costs(B, cfg)
         if has_frz and has_ord:

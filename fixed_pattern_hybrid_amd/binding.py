@@ -75,6 +75,7 @@ class SafParams(ctypes.Structure):
         ("kv_heads", ctypes.c_int32),
         ("logz", ctypes.c_void_p),
         ("qk_packed", ctypes.c_int32),
+        ("fused_dq", ctypes.c_int32),
     ]
 
 
@@ -386,9 +387,12 @@ def saf_hybrid_attn_fwd_noalloc(q, k, v, frozen, a, r, out, lse, softmax_scale=N
 
 def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
                         dq=None, dk=None, dv=None, workspace=None, stream=None, events=None,
-                        qk_packed=False):
+                        qk_packed=False, fused_dq=False):
     """Backward of the hybrid layer; returns (dQ, dK, dV).  qk_packed: q, k,
-    dq and dk hold only the ordinary heads ([B, n_ordinary, T, D])."""
+    dq and dk hold only the ordinary heads ([B, n_ordinary, T, D]).
+    fused_dq: one key-block pass also accumulates dQ with fp32 atomic adds
+    (bf16, D = 64; dQ not bitwise reproducible) instead of a separate
+    query-block pass."""
     packed = bool(qk_packed)
     n_ord = _n_ordinary(frozen)
     if packed:
@@ -416,6 +420,7 @@ def saf_hybrid_attn_bwd(q, k, v, o, dout, lse, frozen, a, r, softmax_scale=None,
     dv = mk(H) if dv is None else dv
     prm = Params(v, frozen, a.shape[1], softmax_scale, events)
     prm.p.qk_packed = 1 if packed else 0
+    prm.p.fused_dq = 1 if fused_dq else 0
     qk = {} if (packed and n_ord == 0) else dict(q=q, k=k, dq=dq, dk=dk)
     prm.set_strides(v=v, o=o, do=dout, dv=dv, **qk)
     if packed and n_ord == 0:

@@ -44,6 +44,7 @@ int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   if (std::isnan(p->softmax_scale) || std::isinf(p->softmax_scale)) return SAF_EINVAL;
   if (!p->frozen) return SAF_EINVAL;
   if (p->qk_packed != 0 && p->qk_packed != 1) return SAF_EINVAL;
+  if (p->fused_dq != 0 && p->fused_dq != 1) return SAF_EINVAL;
   if (p->n_stage_events < 0 || (p->n_stage_events > 0 && !p->stage_events)) return SAF_EINVAL;
   int o = 0, f = 0;
   for (int h = 0; h < p->H; ++h) {
@@ -57,7 +58,8 @@ int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   if ((int64_t)p->B * p->H * p->T > (int64_t)1 << 40) return SAF_EUNSUPPORTED;
   if (p->dtype == SAF_BF16) {
     // one-dimensional grids of at most B * H * ceil(T / 128) programs
-    if ((int64_t)p->B * p->H * ((p->T + 127) / 128) > INT32_MAX) return SAF_EUNSUPPORTED;
+    // (program slots per block rank are rounded up to a multiple of 8)
+    if ((int64_t)(p->B * p->H + 7) * ((p->T + 127) / 128) > INT32_MAX) return SAF_EUNSUPPORTED;
   } else if ((int64_t)p->B * p->H > 65535) {
     return SAF_EUNSUPPORTED;  // fp32 kernels put (b, h) in the grid's second dimension
   }
@@ -93,8 +95,12 @@ float resolve_scale(const saf_attn_params* p) {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-size_t bwd_ws_bytes(const saf_attn_params* p) {
-  return round_up((size_t)p->B * p->H * p->T * sizeof(float), 256);
+// delta [B][H][T]; with the fused-dQ schedule also the fp32 dQ accumulator
+// [B][n_ord][T][D].
+size_t bwd_ws_bytes(const saf_attn_params* p, int n_ord) {
+  const size_t delta = round_up((size_t)p->B * p->H * p->T * sizeof(float), 256);
+  if (!p->fused_dq) return delta;
+  return delta + round_up((size_t)p->B * n_ord * p->T * p->D * sizeof(float), 256);
 }
 
 // bf16 forward with frozen heads: normaliser partials, one float2 per
@@ -317,7 +323,7 @@ int32_t saf_version(void) { return kVersion; }
 size_t saf_hybrid_attn_workspace_bytes(const saf_attn_params* p, int for_bwd) {
   int o, f;
   if (check_params(p, &o, &f) != SAF_OK) return 0;
-  return for_bwd ? bwd_ws_bytes(p) : fwd_ws_bytes(p, f);
+  return for_bwd ? bwd_ws_bytes(p, o) : fwd_ws_bytes(p, f);
 }
 
 int saf_hybrid_attn_fwd(const saf_attn_params* p, const void* q, const void* k, const void* v,
@@ -365,7 +371,8 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   if ((st = check_tensor(dv, p->dv_stride, p)) != SAF_OK) return st;
   if (!lse || !aligned(lse, 4)) return SAF_EINVAL;
   if (n_frz > 0 && (!a || !r || !aligned(a, 4) || !aligned(r, 4))) return SAF_EINVAL;
-  const size_t need = bwd_ws_bytes(p);
+  if (p->fused_dq && (p->dtype != SAF_BF16 || p->D != 64)) return SAF_EUNSUPPORTED;
+  const size_t need = bwd_ws_bytes(p, n_ord);
   if (!ws || ws_bytes < need || !aligned(ws, 256)) return SAF_EWORKSPACE;
 
   BwdArgs args;
@@ -382,6 +389,9 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   args.r = r;
   args.lse = lse;
   args.delta = static_cast<float*>(ws);
+  if (p->fused_dq)
+    args.dqacc = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                          round_up((size_t)p->B * p->H * p->T * sizeof(float), 256));
   args.B = p->B;
   args.H = p->H;
   args.T = p->T;
@@ -397,7 +407,10 @@ int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k, 
   Stages stg{p, stream};
   if (stg.mark() != hipSuccess) return SAF_EHIP;
   hipError_t e;
-  if (p->dtype == SAF_BF16) {
+  if (p->dtype == SAF_BF16 && p->fused_dq) {
+    e = saf::launch_bwd_fused_bf16(args, p->D, stream, p->stage_events, p->n_stage_events, &stg.next);
+    if (e != hipSuccess) return SAF_EHIP;
+  } else if (p->dtype == SAF_BF16) {
     // query-block pass (also stores delta), then the mixed key-block pass
     // (which reads delta and writes the frozen heads' zero dQ/dK rows)
     if (n_ord > 0) {

@@ -82,9 +82,13 @@ __device__ __forceinline__ float bf16hi(unsigned u) { return __builtin_bit_cast(
 // ---------------------------------------------------------------------------
 // Key-block pass, ordinary head (b, h, kb).
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int kb, lds_bf16* smem) {
+// FUSED (d = 64 only): the program also accumulates dQ = s dS K of its 128
+// keys into the fp32 workspace A.dqacc with atomic adds (see bwd_kvq_kernel).
+// oi: rank of head h among the ordinary heads (the dqacc slot).
+template <int D, bool FUSED = false>
+__device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int oi, int kb, lds_bf16* smem) {
   using C = BwdCfg<D>;
+  static_assert(!FUSED || D == 64, "the fused dQ programs are built for d = 64");
   const int l = lane_id(), w = wave_id(), hl = l >> 5;
   const int T = A.T;
   const int k0 = kb * kKvBN;
@@ -141,9 +145,44 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     }
     wait_vm_loads();
   };
+  // Fused dQ: per query tile, each wave writes its 32 keys' bf16 dS rows
+  // (key-major, [128 keys][64 queries], padded) into dS buffer bi; after the
+  // tile's barrier, wave w computes the 32x32 block (queries 32*(w&1).., d
+  // 32*(w>>1)..) of dS K over the block's 128 keys -- during the next tile,
+  // reading buffer bi while that tile writes the other one -- and adds it to
+  // dqacc.  The B operands K[128 keys][32 d] of that product stay in
+  // registers (kt); they are read once from a staged copy of the key block.
+  lds_bf16* dsb = smem + 4 * C::TILE + 2 * (2 * kKvBM) * 2;  // after the float rows
+  constexpr int DSB = kKvBN * C::PITCH;                     // elements per dS buffer
+  bf16x8 kt[FUSED ? 8 : 1];
+  const int qh = w & 1, dbw = w >> 1;
+  if constexpr (FUSED) {
+    // the key block, staged in dS buffer 1 (first written by the second tile,
+    // after a barrier that every wave reaches only once it has read kt)
+    TileDma<D, kKvBN, true> kst;
+    kst.init(A.k.st);
+    kst.issue(kg, A.k.st, k0, T, dsb + DSB);
+  }
+
   load_next(qt0 * kKvBM, 0);
   store_next(0);
   __syncthreads();
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kt[ks] = lds_frag_tr<D>(dsb + DSB, 16 * ks, 32 * dbw);
+  }
+  // dQ of the query tile at i0p from dS buffer `buf` (fused programs)
+  auto dq_tile = [&](int buf, int i0p) {
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(lds_frag_tr<D>(dsb + buf * DSB, 16 * ks, 32 * qh), kt[ks], acc);
+    float* dst = A.dqacc + ((int64_t)(b * A.n_ord + oi) * T) * D + 32 * dbw + (l & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int q = i0p + 32 * qh + 8 * (r >> 2) + 4 * hl + (r & 3);
+      if (q < T) __hip_atomic_fetch_add(dst + (int64_t)q * D, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   f32x16 dva[C::NDB], dka[C::NDB];
 #pragma unroll
@@ -165,6 +204,11 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
     const lds_bf16* O = smem + (2 + bi) * C::TILE;
     const lds_f32* ls = fb + bi * kKvBM;
     const lds_f32* nd = fb + (2 + bi) * kKvBM;
+    if constexpr (FUSED) {
+      if (qt > qt0) dq_tile(bi ^ 1, i0 - kKvBM);
+    }
+    // this lane's dS row in buffer bi (fused programs)
+    lds_bf16* dsrow = dsb + bi * DSB + (32 * w + (l & 31)) * C::PITCH + 4 * hl;
     if (!MASK || i0 + kKvBM - 1 >= wk_lo) {
       // The tile's two 32-query halves are processed together (d = 64) or
       // one after the other (larger d, which halves the live S and dP
@@ -212,11 +256,26 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
         for (int st = 2 * c0; st < 2 * (c0 + CG); ++st) {
           const bf16x8 pf = pack_acc8(s[(st >> 1) - c0], 8 * (st & 1));
           const bf16x8 sf = pack_acc8(dp[(st >> 1) - c0], 8 * (st & 1));
+          if constexpr (FUSED) {
+            // queries 16 st + 4 hl + 0..3 and 16 st + 8 + 4 hl + 0..3
+            *(lds_u32x2*)(dsrow + 16 * st) = __builtin_bit_cast(u32x4, sf).xy;
+            *(lds_u32x2*)(dsrow + 16 * st + 8) = __builtin_bit_cast(u32x4, sf).zw;
+          }
 #pragma unroll
           for (int db = 0; db < C::NDB; ++db) {
             dva[db] = mfma32(lds_frag_tr<D>(O, 16 * st, 32 * db), pf, dva[db]);
             dka[db] = mfma32(lds_frag_tr<D>(Q, 16 * st, 32 * db), sf, dka[db]);
           }
+        }
+      }
+    }
+    if constexpr (FUSED) {
+      if (MASK && !(i0 + kKvBM - 1 >= wk_lo)) {
+        // no query of this tile sees the wave's keys: their dS rows are 0
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          *(lds_u32x2*)(dsrow + 16 * st) = u32x2{0u, 0u};
+          *(lds_u32x2*)(dsrow + 16 * st + 8) = u32x2{0u, 0u};
         }
       }
     }
@@ -227,6 +286,7 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
   int qt = qt0;
   for (; qt < qt_full; ++qt) tile(qt, std::true_type{});
   for (; qt < nqt; ++qt) tile(qt, std::false_type{});
+  if constexpr (FUSED) dq_tile((nqt - 1 - qt0) & 1, (nqt - 1) * kKvBM);
   store_rows_t<D>(A.dv, b, h, j, T, dva, 1.f);
   store_rows_t<D>(A.dk, b, hs, j, T, dka, A.scale);
 }
@@ -366,17 +426,99 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 2)) void bwd_kv_kernel(Bwd
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_k = n_ord_prog + A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / per_k;
-  const int rem = blockIdx.x - kb * per_k;
+  const int kb = blockIdx.x / A.slots;
+  const int rem = blockIdx.x - kb * A.slots;
+  if (rem >= per_k) return;  // padding slot
   if (rem < n_ord_prog) {
     const int b = rem / A.n_ord;
-    kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], kb, smem);
+    kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], rem - b * A.n_ord, kb, smem);
   } else {
     const int f = rem - n_ord_prog;
     const int h = A.frz_heads[f / A.n_groups], grp = f % A.n_groups;
     if (A.B - grp * BwdCfg<D>::G >= BwdCfg<D>::G) kv_frozen<D, BwdCfg<D>::G>(A, h, grp, kb, smem);
     else kv_frozen<D, 1>(A, h, grp, kb, smem);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Fused-dQ backward (d = 64): one key-block launch computes dV, dK and, with
+// fp32 atomic adds into the workspace, dQ; no query-block pass.  Launch
+// order: bwd_pre_kernel (delta of the ordinary rows, dqacc := 0), this
+// kernel, dq_convert_kernel (dQ = scale * dqacc in bf16).  The atomic adds
+// make dQ's rounding depend on their order: results are not bitwise
+// reproducible (dK, dV are).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_kvq_kernel(BwdArgs A) {
+  SAF_DYN_LDS(smem);
+  const int n_ord_prog = A.B * A.n_ord;
+  const int per_k = n_ord_prog + A.n_frz * A.n_groups;
+  const int kb = blockIdx.x / A.slots;
+  const int rem = blockIdx.x - kb * A.slots;
+  if (rem >= per_k) return;  // padding slot
+  if (rem < n_ord_prog) {
+    const int b = rem / A.n_ord;
+    kv_ordinary<D, true>(A, b, A.ord_heads[rem - b * A.n_ord], rem - b * A.n_ord, kb, smem);
+  } else {
+    const int f = rem - n_ord_prog;
+    const int h = A.frz_heads[f / A.n_groups], grp = f % A.n_groups;
+    if (A.B - grp * BwdCfg<D>::G >= BwdCfg<D>::G) kv_frozen<D, BwdCfg<D>::G>(A, h, grp, kb, smem);
+    else kv_frozen<D, 1>(A, h, grp, kb, smem);
+  }
+}
+
+// delta_i = sum_d dO[i][d] O[i][d] of the ordinary rows (four threads per
+// row), and the row's dqacc entries set to 0.  Grid: (row blocks of 64,
+// B * n_ord).
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdArgs A) {
+  const int bo = blockIdx.y;
+  const int b = bo / A.n_ord, oi = bo - b * A.n_ord;
+  const int h = A.ord_heads[oi];
+  const int i = blockIdx.x * 64 + (threadIdx.x >> 2);
+  const int t4 = threadIdx.x & 3;
+  float dl = 0.f;
+  if (i < A.T) {
+    const __bf16* og = (const __bf16*)A.o.ptr + (int64_t)b * A.o.sb + (int64_t)h * A.o.sh + (int64_t)i * A.o.st;
+    const __bf16* dg = (const __bf16*)A.dout.ptr + (int64_t)b * A.dout.sb + (int64_t)h * A.dout.sh +
+                       (int64_t)i * A.dout.st;
+#pragma unroll
+    for (int c = t4; c < D / 8; c += 4) {
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, gload16(og + 8 * c));
+      const bf16x8 dv = __builtin_bit_cast(bf16x8, gload16(dg + 8 * c));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = fmaf((float)dv[e], (float)ov[e], dl);
+    }
+  }
+  dl += __shfl_xor(dl, 1, 64);
+  dl += __shfl_xor(dl, 2, 64);
+  if (i < A.T) {
+    if (t4 == 0) A.delta[((int64_t)b * A.H + h) * A.T + i] = dl;
+    float* z = A.dqacc + ((int64_t)bo * A.T + i) * D;
+#pragma unroll
+    for (int c = t4; c < D / 4; c += 4) sstore16(z + 4 * c, u32x4{0u, 0u, 0u, 0u});
+  }
+}
+
+// dQ[b][slot][i] = bf16(scale * dqacc[b][oi][i]): eight entries per thread.
+// Grid: (row blocks of 256 / (D / 8) rows, B * n_ord).
+template <int D>
+__global__ __launch_bounds__(kThreads) void dq_convert_kernel(BwdArgs A) {
+  constexpr int PER_ROW = D / 8;
+  constexpr int ROWS = kThreads / PER_ROW;
+  const int bo = blockIdx.y;
+  const int b = bo / A.n_ord, oi = bo - b * A.n_ord;
+  const int hs = A.qk_slot[A.ord_heads[oi]];
+  const int i = blockIdx.x * ROWS + threadIdx.x / PER_ROW;
+  const int c = threadIdx.x % PER_ROW;
+  if (i >= A.T) return;
+  const float* src = A.dqacc + ((int64_t)bo * A.T + i) * D + 8 * c;
+  const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
+  const float sc = A.scale;
+  const bf16x8 y = pack_bf16x8(x0[0] * sc, x0[1] * sc, x0[2] * sc, x0[3] * sc, x1[0] * sc, x1[1] * sc,
+                               x1[2] * sc, x1[3] * sc);
+  __bf16* dst = (__bf16*)A.dq.ptr + (int64_t)b * A.dq.sb + (int64_t)hs * A.dq.sh + (int64_t)i * A.dq.st + 8 * c;
+  sstore16(dst, __builtin_bit_cast(u32x4, y));
 }
 
 // ---------------------------------------------------------------------------
@@ -387,9 +529,10 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   using C = BwdCfg<D>;
   SAF_DYN_LDS(smem);
   const int per_q = A.B * A.n_ord;
-  const int qrank = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qrank * per_q;
+  const int qrank = blockIdx.x / A.slots;
+  const int rem = blockIdx.x - qrank * A.slots;
   const int qb = A.nqb - 1 - qrank;
+  if (rem >= per_q) return;  // padding slot
   const int b = rem / A.n_ord;
   const int h = A.ord_heads[rem - b * A.n_ord];
 
@@ -432,10 +575,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   }
   dl += xor32(dl);
   if (hl == 0 && i < T) A.delta[rowv] = dl;
-  // dP accumulators start at -delta, so the products yield dP - delta directly
-  f32x16 ndl;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
+  // (delta is subtracted in the softmax step: seeding the dP accumulators
+  // with it would keep 16 more registers live and spill at 3 waves per SIMD)
 
   const int last_key = min(q0 + kQBM, T) - 1;
   const int ntiles = last_key / kQBN + 1;
@@ -471,7 +612,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         s[c] = f32x16{};
-        dp[c] = ndl;
+        dp[c] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < C::NKS; ++ks) {
           s[c] = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s[c]);
@@ -487,7 +628,7 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
             const int jj = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
             if (jj > i) p = 0.f;
           }
-          dp[c][r] = p * dp[c][r];
+          dp[c][r] = p * (dp[c][r] - dl);
         }
       // dQ^T += K^T dS^T
 #pragma unroll
@@ -525,7 +666,8 @@ hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
-  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
+  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
+  const int64_t grid = (int64_t)args.slots * args.nkb;
   if (grid <= 0) return hipSuccess;
   // only the program kinds present need room (less LDS, more blocks per CU)
   const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? C::kv_lds : C::kv_frz_lds) : C::kv_ord_lds;
@@ -537,7 +679,8 @@ template <int D>
 hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
   using C = BwdCfg<D>;
   args.nqb = (args.T + kQBM - 1) / kQBM;
-  const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
+  args.slots = xcd_slots(args.B * args.n_ord);
+  const int64_t grid = (int64_t)args.slots * args.nqb;
   if (grid <= 0) return hipSuccess;
   static const hipError_t attr = set_lds(bwd_q_kernel<D>, C::q_lds);
   if (attr != hipSuccess) return attr;
@@ -546,7 +689,50 @@ hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Fused-dQ sequence (d = 64): pre, key-block programs with dQ, convert.
+hipError_t launch_bwd_fused_d64(BwdArgs args, hipStream_t stream, hipEvent_t* ev, int nev, int* next_ev) {
+  using C = BwdCfg<64>;
+  constexpr size_t lds = C::kv_lds + size_t(2) * kKvBN * C::PITCH * 2;  // + two dS buffers
+  static_assert(lds <= 80 * 1024, "two blocks per CU");
+  static const hipError_t attr = set_lds(bwd_kvq_kernel<64>, lds);
+  if (attr != hipSuccess) return attr;
+  auto mark = [&]() -> hipError_t {
+    hipError_t e = hipSuccess;
+    if (ev && *next_ev < nev) e = hipEventRecord(ev[*next_ev], stream);
+    ++*next_ev;
+    return e;
+  };
+  args.frz_group = C::G;
+  args.n_groups = (args.B + C::G - 1) / C::G;
+  args.nkb = (args.T + kKvBN - 1) / kKvBN;
+  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
+  if (args.n_ord > 0) {
+    hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)((args.T + 63) / 64), (unsigned)(args.B * args.n_ord)),
+                       dim3(kThreads), 0, stream, args);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || (e = mark()) != hipSuccess) return e;
+  }
+  const int64_t grid = (int64_t)args.slots * args.nkb;
+  hipLaunchKernelGGL(bwd_kvq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), lds, stream, args);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || (e = mark()) != hipSuccess) return e;
+  if (args.n_ord > 0) {
+    constexpr int rows = kThreads / (64 / 8);
+    hipLaunchKernelGGL(dq_convert_kernel<64>, dim3((unsigned)((args.T + rows - 1) / rows), (unsigned)(args.B * args.n_ord)),
+                       dim3(kThreads), 0, stream, args);
+    e = hipGetLastError();
+    if (e != hipSuccess || (e = mark()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_bwd_fused_bf16(const BwdArgs& args, int D, hipStream_t stream, hipEvent_t* ev, int nev,
+                                 int* next_ev) {
+  if (D != 64) return hipErrorInvalidValue;
+  return launch_bwd_fused_d64(args, stream, ev, nev, next_ev);
+}
 
 hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream) {
   switch (D) {

@@ -406,9 +406,10 @@ __global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs A) {
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_q = n_ord_prog + A.n_frz * A.n_groups;
-  const int qrank = blockIdx.x / per_q;
-  const int rem = blockIdx.x - qrank * per_q;
+  const int qrank = blockIdx.x / A.slots;
+  const int rem = blockIdx.x - qrank * A.slots;
   const int qb = A.nqb - 1 - qrank;
+  if (rem >= per_q) return;  // padding slot
   if (rem < n_ord_prog) {
     const int b = rem / A.n_ord;
     fwd_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], qb, smem);
@@ -431,7 +432,8 @@ hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nqb = (args.T + kBM - 1) / kBM;
-  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nqb;
+  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
+  const int64_t grid = (int64_t)args.slots * args.nqb;
   if (grid <= 0) return hipSuccess;
   // only the program kinds present need room (less LDS, more blocks per CU)
   const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? lds : C::frz_lds) : C::ord_lds;

@@ -43,6 +43,8 @@ struct FwdArgs {
   int frz_group;     // batch elements per frozen program
   int n_groups;      // ceil(B / frz_group)
   int nqb;           // number of query blocks
+  int slots;         // programs per query-block rank, rounded up to a multiple
+                     // of 8 (slots past the real programs exit at once)
   // bf16 path: normaliser partials (max, sum) in log2 units over groups of
   // lz_group keys, [n_frz][lz_ngroups][T]; the frozen programs merge them
   // and write lse.
@@ -64,12 +66,15 @@ struct BwdArgs {
   const float* r;
   const float* lse;  // [B][H][T]
   float* delta;      // workspace [B][H][T]: rowsum(dO * O) of ordinary heads
+  float* dqacc;      // fused-dQ workspace [B][n_ord][T][D] fp32 (else null)
   int B, H, T, prior_len;
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
   int n_ord, n_frz;
   int frz_group, n_groups;
   int nqb, nkb;      // query / key blocks of the respective passes
+  int slots;         // programs per block rank, rounded up to a multiple of 8
+                     // (slots past the real programs exit at once)
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
   uint8_t is_frozen[kMaxHeads];
@@ -122,6 +127,11 @@ hipError_t launch_lognorm_identity(const LognormArgs& args, hipStream_t stream);
 hipError_t launch_fwd_bf16(const FwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_kv_bf16(const BwdArgs& args, int D, hipStream_t stream);
 hipError_t launch_bwd_q_bf16(const BwdArgs& args, int D, hipStream_t stream);
+// Fused-dQ backward (bf16, d = 64): delta and dqacc := 0, one key-block launch
+// that also accumulates dQ (atomic adds), dQ conversion.  Records ev[*next_ev]
+// after each kernel while *next_ev < nev (and advances *next_ev).
+hipError_t launch_bwd_fused_bf16(const BwdArgs& args, int D, hipStream_t stream, hipEvent_t* ev, int nev,
+                                 int* next_ev);
 
 // fp32 path: one kernel per pass covers both head kinds.
 hipError_t launch_fwd_f32(const FwdArgs& args, int D, hipStream_t stream);
@@ -226,6 +236,15 @@ constexpr int kCalibBM = 128;  // queries per calibration program
 constexpr int kCalibBN = 64;   // keys per calibration tile
 
 hipError_t launch_calib(const CalibArgs& args, int D, hipStream_t stream);
+
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on
+// XCD i mod 8, each with its own L2).  The layer's launches list their
+// programs rank by rank (longest first) with the same program slots in every
+// rank; rounding the slots per rank up to a multiple of 8 keeps each slot --
+// one (batch, head) or (frozen head, batch group) -- on one XCD in every
+// rank, so the K/V or Q/dO tiles a head's programs share stay in one L2.
+constexpr int kXcds = 8;
+inline int xcd_slots(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program

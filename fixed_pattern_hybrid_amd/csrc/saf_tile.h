@@ -115,7 +115,15 @@ struct TileDma {
 
   __device__ __forceinline__ int offset(int k) const {
     const int m = __builtin_amdgcn_readfirstlane(wave_id()) + 4 * k;
-    const int g = 64 * m + lane_id();
+    int lane;
+    if constexpr (kKeep) {
+      lane = lane_id();
+    } else {
+      // recomputed at each use (volatile), so that no per-load constant
+      // stays live between the tiles
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    }
+    const int g = 64 * m + lane;
     const int row = g / NG, pos = g - row * NG;
     return (m >= NI || pos >= D / 8) ? kOob : row * ste * 2 + L::chunk(row, pos) * 16;
   }

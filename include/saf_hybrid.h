@@ -47,8 +47,10 @@
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream) and
  *    the call never synchronises.  A failed launch returns SAF_EHIP; faults
  *    inside a kernel surface at the caller's next synchronisation.
- *  - The library has no mutable global state; concurrent calls on different
- *    streams are safe.  Results are bitwise deterministic (no atomics).
+ *  - Apart from the scratch array of saf_hybrid_attn_fwd_noalloc, the library
+ *    has no mutable global state; concurrent calls on different streams are
+ *    safe.  Results are bitwise deterministic (no atomics), except dQ of the
+ *    fused-dQ backward schedule (saf_attn_params.fused_dq).
  *  - Calls may be recorded by stream capture into a HIP graph: they enqueue
  *    kernel launches only (plus event records when stage events are asked
  *    for), allocate nothing and issue no memset.  Make one call with the
@@ -139,6 +141,15 @@ typedef struct saf_attn_params {
    * head, q, k, dq and dk may be NULL).  v, o, dO and dV always have all
    * heads.  Strides of the packed tensors step over their own heads. */
   int32_t qk_packed;
+  /* Backward schedule (saf_hybrid_attn_bwd; ignored by the other calls).
+   * 0: two passes -- a query-block pass writes dQ, a key-block pass writes dK
+   *    and dV; results are bitwise reproducible.
+   * 1: fused dQ (bf16 with D = 64 only; otherwise SAF_EUNSUPPORTED) -- the
+   *    key-block pass also accumulates dQ into an fp32 workspace with atomic
+   *    adds (no query-block pass, which recomputes the scores); dK and dV are
+   *    bitwise reproducible, dQ is not (its summation order varies).  The
+   *    workspace grows by B * n_ordinary * T * D * 4 bytes. */
+  int32_t fused_dq;
 } saf_attn_params;
 
 /*
@@ -198,6 +209,11 @@ int saf_hybrid_attn_fwd_noalloc(const saf_attn_params* p, const void* q, const v
  *   dv     : gradients of every head (frozen: W^T dO).
  * q, k of frozen heads are not read.  o is read for ordinary heads only.
  * ws: at least saf_hybrid_attn_workspace_bytes(p, 1) bytes, 256-byte aligned.
+ * Kernels (bf16): with p->fused_dq = 0, the query-block pass (dQ and the
+ * rows' delta = sum_d dO O) then one mixed-head key-block launch; with
+ * p->fused_dq = 1, a delta pass (which also clears the dQ accumulator), one
+ * mixed-head key-block launch that also accumulates dQ, and the dQ
+ * conversion to bf16.
  */
 int saf_hybrid_attn_bwd(const saf_attn_params* p, const void* q, const void* k,
                         const void* v, const void* o, const void* dout,

@@ -52,6 +52,14 @@ def test_flop_accounting_per_pair():
     assert f["total"] == 4 * cfg.D * P
 
 
+def test_fused_dq_atomic_bytes():
+    # 124M layer: 32 key blocks of 128, 64 query tiles of 64; key block kb
+    # meets tiles 2kb .. 63, i.e. 64 - 2kb tiles: 1056 in all, for each of
+    # the 8 x 9 ordinary (b, h); each adds a 64 x 64 fp32 block
+    cfg = CONFIGS["gpt2_124m_4k_25pct"]
+    assert bench.pairs_tiles_bytes(cfg) == 8 * 9 * 1056 * 64 * 64 * 4
+
+
 def test_calibration_flop_accounting():
     # shifted-sum update per entry: log2 A (FMA), A log2 A (FMA), A - A0,
     # s1 += d, s2 += d*d (FMA): 2 + 2 + 1 + 1 + 2 flops, the exponential not
