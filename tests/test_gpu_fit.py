@@ -292,6 +292,20 @@ def test_fit_recipe_parity(B, T):
         _check_fitted(T, g, h, P, ref, f"recipe T={T} head {h}")
 
 
+def test_fit_recipe_parity_T1024(B):
+    """The whole recipe (J = 400 Adam steps, lr 0.05; Appendix A.2) at
+    T = 1024 for two heads, against the oracle's own 400-step fit (about 20 s
+    of float64 work per head): the same bars as at the shorter lengths."""
+    T, n = 1024, 2
+    A = _means(n, T, 1024)
+    ea, er, ne = _fit_inputs(A)
+    g = _run_fit(B, ea, er, ne, F.FIT_STEPS)
+    for h in range(n):
+        P = F.fit_target(A[h])
+        ref = _oracle_fit(ea[h], er[h], ne[h], F.FIT_STEPS)
+        _check_fitted(T, g, h, P, ref, f"recipe T={T} head {h}")
+
+
 def test_fit_recovers_compact_target(B):
     """A target that is itself a compact pattern is recovered to fp32
     precision (kappa -> 0, Equation 20 at the optimum)."""
