@@ -58,8 +58,7 @@ int check_params(const saf_attn_params* p, int* n_ord, int* n_frz) {
   if ((int64_t)p->B * p->H * p->T > (int64_t)1 << 40) return SAF_EUNSUPPORTED;
   if (p->dtype == SAF_BF16) {
     // one-dimensional grids of at most B * H * ceil(T / 128) programs
-    // (program slots per block rank are rounded up to a multiple of 8)
-    if ((int64_t)(p->B * p->H + 7) * ((p->T + 127) / 128) > INT32_MAX) return SAF_EUNSUPPORTED;
+    if ((int64_t)p->B * p->H * ((p->T + 127) / 128) > INT32_MAX) return SAF_EUNSUPPORTED;
   } else if ((int64_t)p->B * p->H > 65535) {
     return SAF_EUNSUPPORTED;  // fp32 kernels put (b, h) in the grid's second dimension
   }

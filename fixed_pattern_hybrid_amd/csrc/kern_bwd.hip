@@ -426,9 +426,8 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 2)) void bwd_kv_kernel(Bwd
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_k = n_ord_prog + A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / A.slots;
-  const int rem = blockIdx.x - kb * A.slots;
-  if (rem >= per_k) return;  // padding slot
+  const int kb = blockIdx.x / per_k;
+  const int rem = blockIdx.x - kb * per_k;
   if (rem < n_ord_prog) {
     const int b = rem / A.n_ord;
     kv_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], rem - b * A.n_ord, kb, smem);
@@ -453,9 +452,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_kvq_kernel(BwdArgs A) {
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_k = n_ord_prog + A.n_frz * A.n_groups;
-  const int kb = blockIdx.x / A.slots;
-  const int rem = blockIdx.x - kb * A.slots;
-  if (rem >= per_k) return;  // padding slot
+  const int kb = blockIdx.x / per_k;
+  const int rem = blockIdx.x - kb * per_k;
   if (rem < n_ord_prog) {
     const int b = rem / A.n_ord;
     kv_ordinary<D, true>(A, b, A.ord_heads[rem - b * A.n_ord], rem - b * A.n_ord, kb, smem);
@@ -529,10 +527,9 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   using C = BwdCfg<D>;
   SAF_DYN_LDS(smem);
   const int per_q = A.B * A.n_ord;
-  const int qrank = blockIdx.x / A.slots;
-  const int rem = blockIdx.x - qrank * A.slots;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
   const int qb = A.nqb - 1 - qrank;
-  if (rem >= per_q) return;  // padding slot
   const int b = rem / A.n_ord;
   const int h = A.ord_heads[rem - b * A.n_ord];
 
@@ -666,8 +663,7 @@ hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
-  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
-  const int64_t grid = (int64_t)args.slots * args.nkb;
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
   if (grid <= 0) return hipSuccess;
   // only the program kinds present need room (less LDS, more blocks per CU)
   const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? C::kv_lds : C::kv_frz_lds) : C::kv_ord_lds;
@@ -679,8 +675,7 @@ template <int D>
 hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
   using C = BwdCfg<D>;
   args.nqb = (args.T + kQBM - 1) / kQBM;
-  args.slots = xcd_slots(args.B * args.n_ord);
-  const int64_t grid = (int64_t)args.slots * args.nqb;
+  const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
   if (grid <= 0) return hipSuccess;
   static const hipError_t attr = set_lds(bwd_q_kernel<D>, C::q_lds);
   if (attr != hipSuccess) return attr;
@@ -705,14 +700,13 @@ hipError_t launch_bwd_fused_d64(BwdArgs args, hipStream_t stream, hipEvent_t* ev
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nkb = (args.T + kKvBN - 1) / kKvBN;
-  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
   if (args.n_ord > 0) {
     hipLaunchKernelGGL(bwd_pre_kernel<64>, dim3((unsigned)((args.T + 63) / 64), (unsigned)(args.B * args.n_ord)),
                        dim3(kThreads), 0, stream, args);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (e = mark()) != hipSuccess) return e;
   }
-  const int64_t grid = (int64_t)args.slots * args.nkb;
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nkb;
   hipLaunchKernelGGL(bwd_kvq_kernel<64>, dim3((unsigned)grid), dim3(kThreads), lds, stream, args);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (e = mark()) != hipSuccess) return e;

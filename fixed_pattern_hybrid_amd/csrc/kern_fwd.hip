@@ -44,9 +44,10 @@ struct FwdCfg {
   static constexpr int G = 2;                  // batch elements per frozen program
   static constexpr int TILE = kBN * PITCH;     // elements of one staged tile
   static constexpr int BAND = kBM + kBN;       // r band length (BM + BN - 1, padded)
-  // per buffer: a2[kBN], then 4 copies of the band, copy c shifted by c
+  // per buffer: a2[kBN], then 2 copies of the band, copy c shifted by c
+  // (two, not four: 40.7 KB per frozen program keeps four blocks per CU)
   static constexpr int BSTRIDE = band_stride(BAND);  // distance between band copies
-  static constexpr int FSTRIDE = kBN + 4 * BSTRIDE;
+  static constexpr int FSTRIDE = kBN + 2 * BSTRIDE;
   static constexpr size_t ord_lds = size_t(2) * 2 * TILE * 2;
   static constexpr size_t frz_lds = size_t(2) * G * TILE * 2 + size_t(2) * FSTRIDE * 4;
 };
@@ -250,9 +251,9 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   const int b0 = grp * GL;  // groups are GL batch elements apart
   const int nb = min(G, A.B - b0);
 
-  // LDS: V tiles [buf][gb], then per buffer a2[kBN] and 4 shifted copies of
+  // LDS: V tiles [buf][gb], then per buffer a2[kBN] and 2 shifted copies of
   // the r band (copy c holds band[y + c] at y), so that each lane reads the
-  // four offsets of four consecutive keys with one aligned 16-byte read.
+  // four offsets of four consecutive keys with two aligned 8-byte reads.
   lds_f32* fbase = (lds_f32*)(smem + 2 * GL * C::TILE);
   constexpr int FSTRIDE = C::FSTRIDE;
 
@@ -314,7 +315,7 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   TileDma<D, kBN, true, typename C::L> vdma;
   vdma.init(A.v.st);
   ScalarStage av;
-  BandStage<C::BAND, kThreads> band;
+  BandStage<C::BAND, kThreads, 2> band;
   auto load_next = [&](int j0, int buf) {
 #pragma unroll
     for (int gb = 0; gb < G; ++gb) {
@@ -359,10 +360,10 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
     if (j0 <= wq_hi) {
       // band index of (i, j): (i - q0) - (j - j0) + BN - 1.  For four keys
       // base..base+3 (base a multiple of 4) the offsets are y0+3..y0 with
-      // y0 = xi - base - 3, and y0 mod 4 = (xi + 1) mod 4 is fixed per lane.
+      // y0 = xi - base - 3, and y0 mod 2 = (xi + 1) mod 2 is fixed per lane.
       const int xi = (i - q0) + kBN - 1;
-      const int cpy = (xi + 1) & 3;
-      const lds_f32* rc = rs + cpy * C::BSTRIDE - cpy;  // rc[y] = band[y] for y = 0 mod 4 reads
+      const int cpy = (xi + 1) & 1;
+      const lds_f32* rc = rs + cpy * C::BSTRIDE - cpy;  // rc[y] = band[y] for even-aligned reads
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
         float wv[8];
@@ -370,7 +371,11 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
         for (int hh = 0; hh < 2; ++hh) {
           const int base = 16 * st + 8 * hh + 4 * hl;
           const f32x4 a4 = lds_read_f4(as + base);
-          const f32x4 r4 = lds_read_f4(rc + (xi - base - 3));  // band[y0 .. y0+3]
+          const lds_f32* rp = rc + (xi - base - 3);  // band[y0 .. y0+3]
+          typedef __attribute__((ext_vector_type(2))) float f32x2;
+          const f32x2 rlo = *(const __attribute__((address_space(3))) f32x2*)rp;
+          const f32x2 rhi = *(const __attribute__((address_space(3))) f32x2*)(rp + 2);
+          const f32x4 r4 = {rlo[0], rlo[1], rhi[0], rhi[1]};
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             wv[4 * hh + k] = EXACT ? fast_exp2(a4[k] + r4[3 - k] - z2) : a4[k] * r4[3 - k];
@@ -402,14 +407,13 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
 // programs, and ranks run longest query blocks first.  The head-state flag
 // (which list the slot falls in) selects the program body.
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_kernel(FwdArgs A) {
+__global__ __launch_bounds__(kThreads, (D == 64 ? 4 : 1)) void fwd_kernel(FwdArgs A) {
   SAF_DYN_LDS(smem);
   const int n_ord_prog = A.B * A.n_ord;
   const int per_q = n_ord_prog + A.n_frz * A.n_groups;
-  const int qrank = blockIdx.x / A.slots;
-  const int rem = blockIdx.x - qrank * A.slots;
+  const int qrank = blockIdx.x / per_q;
+  const int rem = blockIdx.x - qrank * per_q;
   const int qb = A.nqb - 1 - qrank;
-  if (rem >= per_q) return;  // padding slot
   if (rem < n_ord_prog) {
     const int b = rem / A.n_ord;
     fwd_ordinary<D>(A, b, A.ord_heads[rem - b * A.n_ord], qb, smem);
@@ -432,8 +436,7 @@ hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
   args.nqb = (args.T + kBM - 1) / kBM;
-  args.slots = xcd_slots(args.B * args.n_ord + args.n_frz * args.n_groups);
-  const int64_t grid = (int64_t)args.slots * args.nqb;
+  const int64_t grid = (int64_t)(args.B * args.n_ord + args.n_frz * args.n_groups) * args.nqb;
   if (grid <= 0) return hipSuccess;
   // only the program kinds present need room (less LDS, more blocks per CU)
   const size_t need = args.n_frz > 0 ? (args.n_ord > 0 ? lds : C::frz_lds) : C::ord_lds;

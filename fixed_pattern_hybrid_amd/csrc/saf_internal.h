@@ -43,8 +43,6 @@ struct FwdArgs {
   int frz_group;     // batch elements per frozen program
   int n_groups;      // ceil(B / frz_group)
   int nqb;           // number of query blocks
-  int slots;         // programs per query-block rank, rounded up to a multiple
-                     // of 8 (slots past the real programs exit at once)
   // bf16 path: normaliser partials (max, sum) in log2 units over groups of
   // lz_group keys, [n_frz][lz_ngroups][T]; the frozen programs merge them
   // and write lse.
@@ -73,8 +71,6 @@ struct BwdArgs {
   int n_ord, n_frz;
   int frz_group, n_groups;
   int nqb, nkb;      // query / key blocks of the respective passes
-  int slots;         // programs per block rank, rounded up to a multiple of 8
-                     // (slots past the real programs exit at once)
   uint8_t ord_heads[kMaxHeads];
   uint8_t frz_heads[kMaxHeads];
   uint8_t is_frozen[kMaxHeads];
@@ -236,15 +232,6 @@ constexpr int kCalibBM = 128;  // queries per calibration program
 constexpr int kCalibBN = 64;   // keys per calibration tile
 
 hipError_t launch_calib(const CalibArgs& args, int D, hipStream_t stream);
-
-// Workgroups are dispatched to the 8 XCDs round-robin (workgroup i runs on
-// XCD i mod 8, each with its own L2).  The layer's launches list their
-// programs rank by rank (longest first) with the same program slots in every
-// rank; rounding the slots per rank up to a multiple of 8 keeps each slot --
-// one (batch, head) or (frozen head, batch group) -- on one XCD in every
-// rank, so the K/V or Q/dO tiles a head's programs share stay in one L2.
-constexpr int kXcds = 8;
-inline int xcd_slots(int n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 // Tile geometry of the bf16 kernels (used by the host for grid sizes).
 constexpr int kFwdBM = 128;     // queries per forward program

@@ -24,24 +24,25 @@ struct ScalarStage {
   }
 };
 
-// Distance in floats between the four copies of a band: the smallest value
-// >= BAND that is 16 (mod 64).  A wave reads the copies with 16-byte loads
-// whose copy index follows the lane's position mod 4; with copies 4 granules
-// apart in bank order (64 banks of 4 bytes), 16 consecutive lanes touch each
-// bank at most twice (copies a multiple of 64 floats apart share banks:
-// 4-way conflicts).
+// Distance in floats between the copies of a band: the smallest value
+// >= BAND that is 16 (mod 64).  A wave reads the copies with 16-byte (or
+// 8-byte) loads whose copy index follows the lane's position; with copies 4
+// granules apart in bank order (64 banks of 4 bytes), 16 consecutive lanes
+// touch each bank at most twice (copies a multiple of 64 floats apart share
+// banks: 4-way conflicts).
 constexpr int band_stride(int band) { return (band + 47) / 64 * 64 + 16; }
 
 // The relative-position band of a frozen tile, band[x] = log2(e) * r[dmin + x]
 // for x in [0, BAND) (-inf where dmin + x falls outside [0, T)), stored in LDS
-// as four copies STRIDE floats apart: copy c holds band[y + c] at y (-inf past
-// the band's end), so that aligned 16-byte reads fetch four consecutive
-// offsets in any phase.  Thread x loads band[x] once and writes it into every
-// copy that holds it.
-template <int BAND, int NTHR>
+// as NCOPY copies STRIDE floats apart: copy c holds band[y + c] at y (-inf
+// past the band's end), so that aligned reads of NCOPY floats fetch NCOPY
+// consecutive offsets in any phase (four copies: one 16-byte read for four
+// offsets; two copies: two 8-byte reads).  Thread x loads band[x] once and
+// writes it into every copy that holds it.
+template <int BAND, int NTHR, int NCOPY = 4>
 struct BandStage {
   static constexpr int STRIDE = band_stride(BAND);
-  static_assert(BAND + 3 <= NTHR, "one band entry per thread");
+  static_assert(BAND + NCOPY - 1 <= NTHR, "one band entry per thread");
   static_assert(STRIDE >= BAND && STRIDE % 4 == 0, "copies keep 16-byte alignment");
   float v;
   bool valid;
@@ -54,10 +55,10 @@ struct BandStage {
   }
   __device__ __forceinline__ void store(lds_f32* rs) const {
     const int x = threadIdx.x;
-    if (x < BAND + 3) {
+    if (x < BAND + NCOPY - 1) {
       const float val = valid ? v * kLog2e : kNegInf;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NCOPY; ++c) {
         const int y = x - c;
         if (y >= 0 && y < BAND) rs[c * STRIDE + y] = val;
       }
@@ -66,10 +67,10 @@ struct BandStage {
   // The same copies holding 2^(log2(e) r - shift) (0 outside [0, T)).
   __device__ __forceinline__ void store_exp(lds_f32* rs, float shift) const {
     const int x = threadIdx.x;
-    if (x < BAND + 3) {
+    if (x < BAND + NCOPY - 1) {
       const float val = valid ? fast_exp2(v * kLog2e - shift) : 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < NCOPY; ++c) {
         const int y = x - c;
         if (y >= 0 && y < BAND) rs[c * STRIDE + y] = val;
       }
