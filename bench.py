@@ -58,8 +58,19 @@ def flops(cfg, n_ord=None, n_frz=None, B=None):
 
 
 DEFAULT_CONFIG = "gpt2_124m_4k_25pct"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_kv_gpt2-124m-layer_B8_T4096_d64_25pct.txt")
-KERNEL_SOURCES = ("kern_bwd.hip", "saf_device.h", "saf_tile.h", "saf_internal.h")
+# HBM traffic of each layer kernel at the headline workload, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counters (one summary per kernel under profiles/),
+# and the sources each kernel is compiled from: a summary counts only while
+# those sources hash to the value recorded in it.
+TRAFFIC_FILES = {n: os.path.join(ROOT, "profiles", f"traffic_{n}_gpt2-124m-layer_B8_T4096_d64_25pct.txt")
+                 for n in ("fwd", "bwd_q", "bwd_kv")}
+KERNEL_NAMES = {"fwd": "fwd_kernel<64>", "bwd_q": "bwd_q_kernel<64>", "bwd_kv": "bwd_kv_kernel<64>"}
+_COMMON_SOURCES = ("saf_device.h", "saf_tile.h", "saf_internal.h")
+KERNEL_SOURCES = {"fwd": ("kern_fwd.hip",) + _COMMON_SOURCES,
+                  "bwd_q": ("kern_bwd.hip",) + _COMMON_SOURCES,
+                  "bwd_kv": ("kern_bwd.hip",) + _COMMON_SOURCES}
+# algorithmic HBM bytes per launch at the headline workload (each tensor
+# read or written once; see algorithmic_bytes)
 
 
 # Measured v_exp_f32 issue time on gfx950: 3.9 ns per wave instruction per
@@ -84,34 +95,57 @@ def exp_counts(cfg, with_bwd: bool):
     return {"count": n, "fwd": fwd, "bwd": bwd, "bound_ms": round(n / EXP_PER_S * 1e3, 4)}
 
 
-def kernel_source_sha() -> str:
-    """Hash of the sources the key-block kernel is compiled from."""
+def kernel_source_sha(name: str = "bwd_kv") -> str:
+    """Hash of the sources layer kernel `name` (fwd, bwd_q, bwd_kv) is
+    compiled from."""
     import hashlib
 
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "fixed_pattern_hybrid_amd", "csrc", name), "rb") as f:
+    for src in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "fixed_pattern_hybrid_amd", "csrc", src), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when it was taken on other kernel sources (or is absent)."""
-    if not os.path.exists(TRAFFIC_FILE):
+def measured_traffic(name: str):
+    """HBM bytes per launch of layer kernel `name` from its committed counter
+    summary, or None when that was taken on other kernel sources (or is
+    absent)."""
+    path = TRAFFIC_FILES.get(name)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 key, val = line.split(":", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("kernel") != kernel or kv.get("source_sha") != kernel_source_sha():
+    if kv.get("kernel") != KERNEL_NAMES[name] or kv.get("source_sha") != kernel_source_sha(name):
         return None
     try:
         return int(float(kv["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def algorithmic_bytes(cfg):
+    """Minimum HBM bytes per launch of each layer kernel (bf16 tensors read
+    or written once): forward -- Q, K of ordinary heads, V, O, lse, a, r;
+    query-block pass -- Q, K, V, O, dO of ordinary heads, lse, delta, dQ;
+    key-block pass -- Q, K, V, dO of ordinary heads, dO of frozen heads, lse,
+    delta, dK, dV, the frozen heads' zero dQ/dK rows, a, r."""
+    n_frz = len(cfg.frozen)
+    n_ord = cfg.H - n_frz
+    e = 2 if cfg.dtype == "bf16" else 4
+    t_ord = cfg.B * n_ord * cfg.T * cfg.D * e  # one tensor's ordinary heads
+    t_frz = cfg.B * n_frz * cfg.T * cfg.D * e
+    row = cfg.B * cfg.H * cfg.T * 4            # one fp32 value per (b, h, t)
+    ar = 2 * n_frz * cfg.T * 4
+    return {
+        "fwd": 2 * t_ord + 2 * (t_ord + t_frz) + row + ar,
+        "bwd_q": 6 * t_ord + 2 * row,
+        "bwd_kv": 4 * t_ord + t_frz + 2 * row + 2 * (t_ord + t_frz) + 2 * t_frz + ar,
+    }
 
 
 def calib_copy(n_mib: int = 1024, reps: int = 5):
@@ -724,7 +758,8 @@ def main():
     roof = None
     if dom_flops is not None:
         ach = dom_flops / (kern_ms[dom] * 1e-3) / 1e12
-        traffic = measured_traffic(f"bwd_kv_kernel<{D}>") if dom == "bwd_kv" else None
+        headline = args.config == DEFAULT_CONFIG
+        traffic = measured_traffic(dom) if headline else None
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dom,
                 "kernel_ms": round(kern_ms[dom], 4)}
@@ -759,6 +794,20 @@ def main():
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }
+    if args.config == DEFAULT_CONFIG:
+        # HBM traffic of every layer kernel (counter summaries) against its
+        # algorithmic bytes, and the bandwidth it implies at this run's times
+        alg = algorithmic_bytes(cfg)
+        hbm = {}
+        for n in ("fwd", "bwd_q", "bwd_kv"):
+            if n not in kern_ms:
+                continue
+            tb = measured_traffic(n)
+            hbm[n] = {"algorithmic_bytes": alg[n], "traffic_bytes": tb,
+                      "traffic_over_algorithmic": round(tb / alg[n], 3) if tb else None,
+                      "traffic_GBps": round(tb / (kern_ms[n] * 1e-3) / 1e9, 1) if tb else None,
+                      "frac_of_hbm_peak": round(tb / (kern_ms[n] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if tb else None}
+        out["hbm_traffic"] = hbm
     if not args.no_pattern_grad and do is not None and has_frz:
         tp = trainable_pattern_leg(B, cfg, dict(v=v, o=o, do=do, lse=lse, a=a, r=r, fz=fz), stream)
         tp["over_layer_step"] = round(tp["ms"] / ms, 4)
