@@ -201,6 +201,21 @@ def per_head_costs(B, cfg, reps: int = 10):
     def q(xs, p):
         return float(np.percentile(np.asarray(xs) / cfg.H, p))
 
+    # the frozen heads' forward with their normalisers given (stored with the
+    # pattern, as the pages keep log Z beside alpha and rho)
+    fr = res["frozen"]
+    fr["logz"] = B.saf_pattern_lognorm(fr["a"], fr["r"], cfg.T)
+
+    def run_fwd_logz(t):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            B.saf_hybrid_attn_fwd(t["q"], t["k"], t["v"], t["fz"], t["a"], t["r"], out=t["o"], lse=t["lse"],
+                                  workspace=t["ws"], logz=t["logz"])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     out = {}
     for with_bwd, tag in ((False, "fwd"), (True, "fwd_bwd")):
         run(res["ordinary"], with_bwd)
@@ -217,6 +232,16 @@ def per_head_costs(B, cfg, reps: int = 10):
                     "ordinary_iqr": o_iqr, "frozen_iqr": f_iqr,
                     # frozen median below the ordinary one with disjoint interquartile ranges
                     "frozen_cheaper": bool(f_ms < o_ms and f_iqr[1] < o_iqr[0])}
+    run(res["ordinary"], False)
+    run_fwd_logz(fr)
+    sz = {"ordinary": [], "frozen": []}
+    for order in (("ordinary", "frozen"), ("frozen", "ordinary")) * 4:
+        for kind in order:
+            sz[kind].append(run(res["ordinary"], False) if kind == "ordinary" else run_fwd_logz(fr))
+    o_ms, f_ms = q(sz["ordinary"], 50), q(sz["frozen"], 50)
+    out["fwd_stored_lognorm"] = {"ordinary_ms_per_head": round(o_ms, 5), "frozen_ms_per_head": round(f_ms, 5),
+                                 "frozen_over_ordinary": round(f_ms / o_ms, 3),
+                                 "note": "forward only, the frozen heads' log N given (no normaliser pass)"}
     # zero-replacement control: the same all-ordinary call against itself in
     # A-B-B-A order; the comparison above is trusted only if this stays ~1.00
     ctl = {"a": [], "b": []}

@@ -180,7 +180,8 @@ __device__ __forceinline__ void kv_ordinary(const BwdArgs& A, int b, int h, int 
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int q = i0p + 32 * qh + 8 * (r >> 2) + 4 * hl + (r & 3);
-      if (q < T) __hip_atomic_fetch_add(dst + (int64_t)q * D, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (q < T)
+        __hip_atomic_fetch_add(dst + (int64_t)q * D, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
 
