@@ -649,17 +649,12 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   store_rows_t<D>(A.dq, b, hs, i, T, dqa, A.scale);
 }
 
-template <typename K>
-hipError_t set_lds(K kernel, size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-}
 
 template <int D>
 hipError_t launch_kv_d(BwdArgs args, hipStream_t stream) {
   using C = BwdCfg<D>;
   static_assert(C::kv_lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = set_lds(bwd_kv_kernel<D>, C::kv_lds);
+  const hipError_t attr = ensure_dynamic_lds<bwd_kv_kernel<D>>(C::kv_lds);
   if (attr != hipSuccess) return attr;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;
@@ -678,7 +673,7 @@ hipError_t launch_q_d(BwdArgs args, hipStream_t stream) {
   args.nqb = (args.T + kQBM - 1) / kQBM;
   const int64_t grid = (int64_t)args.B * args.n_ord * args.nqb;
   if (grid <= 0) return hipSuccess;
-  static const hipError_t attr = set_lds(bwd_q_kernel<D>, C::q_lds);
+  const hipError_t attr = ensure_dynamic_lds<bwd_q_kernel<D>>(C::q_lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(bwd_q_kernel<D>, dim3((unsigned)grid), dim3(kThreads), C::q_lds, stream,
                      args);
@@ -690,7 +685,7 @@ hipError_t launch_bwd_fused_d64(BwdArgs args, hipStream_t stream, hipEvent_t* ev
   using C = BwdCfg<64>;
   constexpr size_t lds = C::kv_lds + size_t(2) * kKvBN * C::PITCH * 2;  // + two dS buffers
   static_assert(lds <= 80 * 1024, "two blocks per CU");
-  static const hipError_t attr = set_lds(bwd_kvq_kernel<64>, lds);
+  const hipError_t attr = ensure_dynamic_lds<bwd_kvq_kernel<64>>(lds);
   if (attr != hipSuccess) return attr;
   auto mark = [&]() -> hipError_t {
     hipError_t e = hipSuccess;

@@ -430,8 +430,7 @@ hipError_t launch_fwd_d(FwdArgs args, hipStream_t stream) {
   using C = FwdCfg<D>;
   constexpr size_t lds = C::ord_lds > C::frz_lds ? C::ord_lds : C::frz_lds;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(fwd_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t attr = ensure_dynamic_lds<fwd_kernel<D>>(lds);
   if (attr != hipSuccess) return attr;
   args.frz_group = C::G;
   args.n_groups = (args.B + C::G - 1) / C::G;

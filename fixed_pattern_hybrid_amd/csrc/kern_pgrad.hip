@@ -364,8 +364,7 @@ template <int D>
 hipError_t launch_pgrad_bf16_d(PgradArgs args, hipStream_t stream) {
   using C = PgCfg<D>;
   static_assert(C::lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(pg_kv_kernel<D>), hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::lds);
+  const hipError_t attr = ensure_dynamic_lds<pg_kv_kernel<D>>(C::lds);
   if (attr != hipSuccess) return attr;
   const int64_t grid = (int64_t)args.nch * args.nkb * args.n_frz * args.n_groups;
   if (grid <= 0) return hipSuccess;

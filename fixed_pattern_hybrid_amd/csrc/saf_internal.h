@@ -5,7 +5,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace saf {
+
+// A kernel that uses more than 64 KB of dynamic LDS needs its attribute
+// raised once per device.  The result is remembered per (kernel, device)
+// only when it succeeds, so a failed attempt is retried by the next call.
+template <auto Kernel>
+hipError_t ensure_dynamic_lds(size_t bytes) {
+  static std::atomic<uint64_t> done{0};  // one bit per device index < 64
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 constexpr int kMaxHeads = 256;
 constexpr int kLognormChunk = 256;     // keys per step of a normaliser block

@@ -47,15 +47,17 @@
  *  - Work is enqueued asynchronously on `stream` (0 = the null stream) and
  *    the call never synchronises.  A failed launch returns SAF_EHIP; faults
  *    inside a kernel surface at the caller's next synchronisation.
- *  - Apart from the scratch array of saf_hybrid_attn_fwd_noalloc, the library
- *    has no mutable global state; concurrent calls on different streams are
- *    safe.  Results are bitwise deterministic (no atomics), except dQ of the
+ *  - Apart from the scratch array of saf_hybrid_attn_fwd_noalloc and a
+ *    per-device record of which kernels' LDS attribute is set (atomic), the
+ *    library has no mutable global state; concurrent calls on different
+ *    streams are safe.  Results are bitwise deterministic (no atomics), except dQ of the
  *    fused-dQ backward schedule (saf_attn_params.fused_dq).
  *  - Calls may be recorded by stream capture into a HIP graph: they enqueue
  *    kernel launches only (plus event records when stage events are asked
  *    for), allocate nothing and issue no memset.  Make one call with the
- *    same head dimension and dtype outside capture first: it sets each
- *    kernel's LDS size attribute once per process.
+ *    same head dimension and dtype outside capture first on each device: it
+ *    sets each kernel's LDS size attribute once per device (a failed attempt
+ *    is not remembered and is retried by the next call).
  */
 #ifndef SAF_HYBRID_H
 #define SAF_HYBRID_H
