@@ -22,8 +22,6 @@ from _helpers import (
     forward_rounding_sigma, host, max_abs, out_max_abs, rel_l2, say, to_dev,
 )
 
-pytestmark = pytest.mark.gpu
-
 N_OPS = 50
 FUZZ_SEED = 20260  # generator of the operations (inputs use their own seeds)
 PG_F32_RELL2 = 1e-4
@@ -65,7 +63,7 @@ def draw_ops(n=N_OPS, seed=FUZZ_SEED):
 
 
 def test_fuzz_ops_cover_the_options():
-    # host-only check of the draw itself: every option occurs
+    # host-only check of the draw itself (runs without a GPU): every option occurs
     ops = draw_ops()
     assert len(ops) == N_OPS
     for key in ("strided", "packed", "logz", "pgrad"):
@@ -170,6 +168,7 @@ def run_op(B, op):
             assert np.all(da[h, cfg.T:] == 0.0) and np.all(dr[h, cfg.T:] == 0.0)
 
 
+@pytest.mark.gpu
 def test_fuzz_50_operations(B):
     for op in draw_ops():
         say(f"fuzz op {op['idx']}: {op}")
