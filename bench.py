@@ -662,7 +662,8 @@ def cpu_baseline(cfg, inp, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    # at least 200 ms of timed work at the headline shape (0.84 ms per step)
+    ap.add_argument("--steps", type=int, default=250)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default=DEFAULT_CONFIG,
                     help="workload (synth.CONFIGS key); the default is the headline metric's; others: "

@@ -271,12 +271,12 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
     float M = kNegInf, S = 0.f;
     const float2* part = A.lz_part + (int64_t)hidx * A.lz_ngroups * T + i;
     const int cmax = i / A.lz_group;  // groups 0..cmax hold this row's terms
-    for (int c0 = 0; c0 <= cmax; c0 += 4) {
-      float2 p[4];
+    for (int c0 = 0; c0 <= cmax; c0 += 8) {
+      float2 p[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) p[u] = part[(int64_t)min(c0 + u, cmax) * T];  // four loads in flight
+      for (int u = 0; u < 8; ++u) p[u] = part[(int64_t)min(c0 + u, cmax) * T];  // eight loads in flight
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         if (c0 + u <= cmax && p[u].y > 0.f) {
           const float Mn = fmaxf(M, p[u].x);
           S = S * fast_exp2(M - Mn) + p[u].y * fast_exp2(p[u].x - Mn);
@@ -299,10 +299,23 @@ __device__ __forceinline__ void fwd_frozen(const FwdArgs& A, int hidx, int grp, 
   // block must have f_i <= 2^90 (terms that underflow are then below 2^-36
   // of their row); otherwise (a and r whose ranges are far apart) the block
   // takes the exponential per weight.
+  // (offsets 0 .. last_key are the block's; eight strides of loads are
+  // issued before any is awaited, at addresses clamped to last_key, which
+  // leaves the maxima unchanged)
   float ca = kNegInf, cr = kNegInf;
-  for (int x = threadIdx.x; x <= last_key; x += kThreads) {
-    ca = fmaxf(ca, arow[x]);
-    cr = fmaxf(cr, rrow[x]);  // offsets 0 .. last_key are the block's
+  for (int x0 = threadIdx.x; x0 <= last_key; x0 += 8 * kThreads) {
+    float av[8], rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int x = min(x0 + u * kThreads, last_key);
+      av[u] = arow[x];
+      rv[u] = rrow[x];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ca = fmaxf(ca, av[u]);
+      cr = fmaxf(cr, rv[u]);
+    }
   }
   ca = block_max(ca, fbase) * kLog2e;
   cr = block_max(cr, fbase) * kLog2e;
