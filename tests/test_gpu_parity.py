@@ -223,6 +223,39 @@ def test_graph_capture_replays_match_eager(B):
         torch.cuda.synchronize()
 
 
+def test_concurrent_calls_on_two_streams(B):
+    # No mutable global state on the workspace entry points: two layers'
+    # forward + backward enqueued on two streams at once (each with its own
+    # workspace) give exactly their sequential results.
+    cfgs = [CONFIGS["pages_check_t129"].with_(B=3, T=600, prior_len=None, name="stream_a"),
+            CONFIGS["pages_check_t129"].with_(B=2, H=6, T=900, prior_len=None, frozen=(0, 2, 3), name="stream_b")]
+    runs = []
+    for c in cfgs:
+        inp = make_inputs(c, with_do=True)
+        dev = upload(inp)
+        fz = [int(x) for x in inp.frozen]
+        O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+        G = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"])
+        torch.cuda.synchronize()
+        runs.append((dev, fz, (O, L) + tuple(G)))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [None, None]
+    for rep in range(3):
+        for s_ in streams:
+            s_.wait_stream(torch.cuda.current_stream())
+        for x, (dev, fz, _) in enumerate(runs):
+            with torch.cuda.stream(streams[x]):
+                O, L = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"],
+                                             stream=streams[x])
+                G = B.saf_hybrid_attn_bwd(dev["q"], dev["k"], dev["v"], O, dev["do"], L, fz, dev["a"], dev["r"],
+                                          stream=streams[x])
+                outs[x] = (O, L) + tuple(G)
+        torch.cuda.synchronize()
+        for x in range(2):
+            for got, ref in zip(outs[x], runs[x][2]):
+                assert torch.equal(got, ref), (rep, x)
+
+
 # --------------------------------------------------------------------------
 # Pattern entry points
 # --------------------------------------------------------------------------

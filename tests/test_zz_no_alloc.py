@@ -115,3 +115,41 @@ def test_noalloc_rejects_shapes_beyond_its_scratch(B):
     assert st == B.SAF_ESCRATCH
     torch.cuda.synchronize()
     assert bool((x == 0).all()) and bool((a == 0).all())
+
+
+def test_noalloc_forward_under_graph_capture(B):
+    # The caller the entry point is for: a forward captured into a HIP graph.
+    # Every replay must equal the eager result, also after eager no-allocation
+    # calls on other inputs have overwritten the shared scratch in between.
+    cfg = CONFIGS["pages_check_t129"].with_(B=2, H=6, T=700, prior_len=None, frozen=(0, 3, 5), name="noalloc_graph")
+    other = cfg.with_(T=900, name="noalloc_graph_other")
+    inp, inp2 = make_inputs(cfg, with_do=False), make_inputs(other, seed=7, with_do=False)
+    dev, dev2 = upload(inp), upload(inp2)
+    fz = [int(x) for x in inp.frozen]
+    O0, L0 = B.saf_hybrid_attn_fwd(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"])
+    O, L = torch.empty_like(O0), torch.empty_like(L0)
+    O2, L2 = torch.empty_like(dev2["v"]), torch.empty((other.B, other.H, other.T), device="cuda")
+
+    def step():
+        B.saf_hybrid_attn_fwd_noalloc(dev["q"], dev["k"], dev["v"], fz, dev["a"], dev["r"], out=O, lse=L)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # first call on the device outside capture (symbol address, LDS attribute)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        O.fill_(float("nan"))
+        L.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        say(f"  replay {rep}")
+        assert torch.equal(O, O0) and torch.equal(L, L0)
+        # eager no-allocation call on other inputs: overwrites the scratch
+        B.saf_hybrid_attn_fwd_noalloc(dev2["q"], dev2["k"], dev2["v"], fz, dev2["a"], dev2["r"], out=O2, lse=L2)
+        torch.cuda.synchronize()
