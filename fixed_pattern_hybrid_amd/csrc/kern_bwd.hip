@@ -333,13 +333,54 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   }
   const float* lse = A.lse + ((int64_t)b0 * A.H + h) * T;  // log N, same for every b
 
-  // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] and 4 shifted copies
-  // of the r band (copy c holds band[y + c] at y)
+  // LDS: dO tiles [buf][gb], then per buffer z2[kKvBM] (or f[kKvBM]) and 4
+  // shifted copies of the r band (copy c holds band[y + c] at y)
   lds_f32* fb = (lds_f32*)(smem + 2 * GL * C::TILE);
   constexpr int FSTRIDE = C::FSTRIDE;
 
   const int qt0 = k0 / kKvBM;
   const int nqt = (T + kKvBM - 1) / kKvBM;
+
+  // Factored weights, as in the forward: W[i][j] = ea[j] er[i-j] f_i with
+  // ea = 2^(a2[j] - ca), er = 2^(r2[d] - cr), f_i = 2^(ca + cr - z2_i), ca
+  // and cr the maxima over the block's keys and over the offsets 0 .. T-1-k0
+  // it meets.  A tile stages er and f, a weight is er * f (one multiply
+  // instead of an exponential) and ea scales the key's dV row at the end.
+  // Taken when every row i >= k0 has f_i <= 2^90 and both maxima are finite
+  // (terms that then underflow are below 2^-36 of their row); otherwise the
+  // program takes the exponential per weight.  Eight strides of loads are
+  // issued before any is awaited, at addresses clamped into range (which
+  // leaves the maxima and the test unchanged).
+  // (d = 96 and 128 keep the exponential: there the factored tiles' extra
+  // registers would spill)
+  const int last_d = T - 1 - k0;  // offsets 0 .. last_d; rows k0 .. T-1
+  bool exact = true;
+  float ea = 1.f, cr = 0.f, cacr = 0.f;
+  if constexpr (D == 64) {
+    float ca = (j < T) ? a2 : kNegInf;
+    cr = kNegInf;
+    for (int x0 = threadIdx.x; x0 <= last_d; x0 += 8 * kThreads) {
+      float rv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) rv[u] = rrow[min(x0 + u * kThreads, last_d)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cr = fmaxf(cr, rv[u]);
+    }
+    ca = block_max(ca, fb);
+    cr = block_max(cr, fb) * kLog2e;
+    const float zlo = ca + cr - 90.f;  // every z2_i must be >= zlo
+    bool bad = !(ca > kNegInf && cr > kNegInf);
+    for (int x0 = threadIdx.x; x0 <= last_d && !bad; x0 += 8 * kThreads) {
+      float zv8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) zv8[u] = lse[k0 + min(x0 + u * kThreads, last_d)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) bad |= !(zv8[u] * kLog2e >= zlo);
+    }
+    exact = __syncthreads_or(bad);
+    if (!exact) ea = fast_exp2(a2 - ca);  // 0 for keys >= T (a2 = -inf)
+    cacr = ca + cr;
+  }
 
   TileDma<D, kKvBM, (D == 64)> odma;
   odma.init(A.dout.st);
@@ -353,18 +394,25 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
   };
   // Next-tile operands: dO tiles, z2 = log N (log2 units) of the tile rows,
   // and the r band over offsets [i0 - k0 - (BN-1), i0 + BM - 1 - k0]; loaded
-  // into registers at the start of a tile, written to LDS at its end.
+  // into registers at the start of a tile, written to LDS at its end.  Band
+  // offsets beyond T-1-k0 (met only by the padding rows of the last tile)
+  // count as outside the pattern, so that er stays <= 1 there.
   ScalarStage zv;
   BandStage<C::BAND, kThreads> band;
   auto load_next = [&](int i0, int buf) {
     load_do(i0, buf);
     zv.load(lse, i0, T);
-    band.load(rrow, i0 - k0 - (kKvBN - 1), T);
+    band.load(rrow, i0 - k0 - (kKvBN - 1), T - k0);
   };
   auto store_next = [&](int buf) {
     lds_f32* zs = fb + buf * FSTRIDE;
-    if (threadIdx.x < kKvBM) zs[threadIdx.x] = zv.valid ? zv.v * kLog2e : __builtin_inff();
-    band.store(zs + kKvBM);
+    if (D != 64 || exact) {
+      if (threadIdx.x < kKvBM) zs[threadIdx.x] = zv.valid ? zv.v * kLog2e : __builtin_inff();
+      band.store(zs + kKvBM);
+    } else {
+      if (threadIdx.x < kKvBM) zs[threadIdx.x] = zv.valid ? fast_exp2(cacr - zv.v * kLog2e) : 0.f;
+      band.store_exp(zs + kKvBM, cr);
+    }
     wait_vm_loads();
   };
 
@@ -378,6 +426,8 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) dva[gb][db] = f32x16{};
 
+  auto tiles = [&](auto exact_tag) {
+  constexpr bool EXACT = decltype(exact_tag)::value;
   for (int qt = qt0; qt < nqt; ++qt) {
     const int i0 = qt * kKvBM;
     const int bi = (qt - qt0) & 1;
@@ -401,7 +451,7 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
           const f32x4 z4 = lds_read_f4(zs + base);
           const f32x4 r4 = lds_read_f4(rc + base + xj);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) wv[4 * hh + k] = fast_exp2(a2 + r4[k] - z4[k]);
+          for (int k = 0; k < 4; ++k) wv[4 * hh + k] = EXACT ? fast_exp2(a2 + r4[k] - z4[k]) : r4[k] * z4[k];
         }
         const bf16x8 wf = pack_bf16x8(wv[0], wv[1], wv[2], wv[3], wv[4], wv[5], wv[6], wv[7]);
 #pragma unroll
@@ -415,9 +465,12 @@ __device__ __forceinline__ void kv_frozen(const BwdArgs& A, int h, int grp, int 
     if (more) store_next(bi ^ 1);
     __syncthreads();
   }
+  };
+  if (exact) tiles(std::true_type{});
+  else if constexpr (D == 64) tiles(std::false_type{});
 #pragma unroll
   for (int gb = 0; gb < G; ++gb)
-    if (gb < nb) store_rows_t<D>(A.dv, b0 + gb, h, j, T, dva[gb], 1.f);
+    if (gb < nb) store_rows_t<D>(A.dv, b0 + gb, h, j, T, dva[gb], ea);
 }
 
 // Key-block pass for every head in one launch: program p -> (key block, slot),
