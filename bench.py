@@ -16,6 +16,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -79,18 +80,19 @@ EXP_PER_S = 64 / 3.9e-9 * 1024
 
 
 def exp_counts(cfg, with_bwd: bool):
-    """Exponentials per step as this design computes them (ordinary heads:
-    one per causal pair and (b, h) in the forward and one in each of the
-    backward's two recomputing passes; frozen heads: one per pair, shared by
-    a batch group of two, in the forward and in the backward's dV; the
-    normalisers' T(T+1)/2 per frozen head), and the time they take at the
-    measured exponential rate."""
+    """Exponentials per step as this design computes them, for patterns
+    whose ranges pass the factored-weight test (the synthetic ones do):
+    ordinary heads take one per causal pair and (b, h) in the forward and one
+    in each of the backward's two recomputing passes; frozen heads build
+    their weights and normalisers from factored exponentials (one multiply
+    per pair), except the backward's dV at d != 64, one per pair shared by a
+    batch group of two.  Also the time they take at the measured rate."""
     P = pairs(cfg.T)
     n_frz = len(cfg.frozen)
     n_ord = cfg.H - n_frz
     groups = (cfg.B + 1) // 2
-    fwd = P * cfg.B * n_ord + P * groups * n_frz + P * n_frz
-    bwd = (2 * P * cfg.B * n_ord + P * groups * n_frz) if with_bwd else 0
+    fwd = P * cfg.B * n_ord
+    bwd = (2 * P * cfg.B * n_ord + (0 if cfg.D == 64 else P * groups * n_frz)) if with_bwd else 0
     n = fwd + bwd
     return {"count": n, "fwd": fwd, "bwd": bwd, "bound_ms": round(n / EXP_PER_S * 1e3, 4)}
 
@@ -299,6 +301,51 @@ def trainable_pattern_leg(B, cfg, t, stream, reps: int = 20):
                          "flops_per_launch": fl},
             "note": "gradients of a and r for the frozen heads (trainable-pattern variant), one call per "
                     "step after the layer's backward; not included in value"}
+
+
+def fit_scaling_leg(B, stream, n_heads: int = 12, Ts=(4096, 8192, 16384, 32768, 65536), steps: int = 400):
+    """Cost of the compact-pattern fit as T grows: the recipe's 400 Adam
+    steps on n_heads heads whose targets are the marginals of uniform causal
+    attention (P[i][j] = 1/(i+1), so eta_abs[j] = eta_rel[j] = H_T - H_j in
+    closed form, H the harmonic numbers, and sum P ln P = -ln T!, which gives
+    kappa, the mean row KL of the fitted pattern from P; a compact pattern
+    with a and r of equal slope is uniform, so kappa -> 0).  Every step evaluates the row
+    normalisers and both fitted marginals exactly, over every causal pair, so
+    the time grows as T^2; the target values do not change that work."""
+    import numpy as np
+    import torch
+
+    rows = []
+    for T in Ts:
+        H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1, dtype=np.float64))])
+        eta = torch.from_numpy((H[T] - H[:T]).astype(np.float32)).cuda()
+        eta_abs = eta.expand(n_heads, T).contiguous()
+        eta_rel = eta_abs.clone()
+        negent = torch.full((n_heads,), -math.lgamma(T + 1.0), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(B.fit_pattern_workspace_bytes(n_heads, T), 256), dtype=torch.uint8, device="cuda")
+
+        def fit(J):
+            return B.saf_fit_pattern(eta_abs, eta_rel, negent, steps=J, workspace=ws, stream=stream)
+
+        out = fit(steps)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        fit(steps)
+        ev[1].record(stream)
+        fit(0)
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        t_fit = ev[0].elapsed_time(ev[1])
+        t_step = (t_fit - ev[1].elapsed_time(ev[2])) / steps
+        pairs_ = T * (T + 1) // 2
+        rows.append({"T": T, "fit_ms": round(t_fit, 3), "adam_step_ms": round(t_step, 5),
+                     "causal_pairs_per_s": float(f"{3 * pairs_ * n_heads / (t_step * 1e-3):.4g}"),
+                     "kappa_max": float(f"{float(out['kappa'].max()):.4g}")})
+        del ws, out
+    return {"heads": n_heads, "adam_steps": steps, "targets": "uniform causal attention (closed form)",
+            "rows": rows,
+            "note": "exact band sums per step (no FFT): time ~ T^2; kappa_max over the heads after the fit"}
 
 
 def pattern_fit_leg(B, stream, reps: int = 5):
@@ -677,6 +724,8 @@ def main():
     ap.add_argument("--no-fit", action="store_true",
                     help="skip the pattern-fitting leg (36 fits at T=4096, reported apart from value)")
     ap.add_argument("--fit-only", action="store_true", help="run only the pattern-fitting leg")
+    ap.add_argument("--fit-scaling", action="store_true",
+                    help="run only the fit's T-scaling leg (12 heads, T = 4096 .. 65536, 400 Adam steps each)")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip the calibration-statistics leg (144 heads, 32 x 4096 tokens, apart from value)")
     ap.add_argument("--calib-only", action="store_true", help="run only the calibration-statistics leg")
@@ -700,6 +749,9 @@ def main():
 
     if args.fit_only:
         print(json.dumps({"pattern_fit": pattern_fit_leg(B, torch.cuda.current_stream())}), flush=True)
+        return
+    if args.fit_scaling:
+        print(json.dumps({"fit_scaling": fit_scaling_leg(B, torch.cuda.current_stream())}), flush=True)
         return
     if args.calib_only:
         print(json.dumps({"calibration": calibration_leg(B, torch.cuda.current_stream())}), flush=True)
