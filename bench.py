@@ -303,6 +303,16 @@ def trainable_pattern_leg(B, cfg, t, stream, reps: int = 20):
                     "step after the layer's backward; not included in value"}
 
 
+def uniform_causal_targets(T: int):
+    """Fit targets of uniform causal attention, P[i][j] = 1/(i+1) for j <= i:
+    eta_abs[j] = eta_rel[j] = sum_{i >= j} 1/(i+1) = H_T - H_j (H the harmonic
+    numbers) and sum P ln P = -sum_i ln(i+1) = -ln T!."""
+    import numpy as np
+
+    H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1, dtype=np.float64))])
+    return H[T] - H[:T], -math.lgamma(T + 1.0)
+
+
 def fit_scaling_leg(B, stream, n_heads: int = 12, Ts=(4096, 8192, 16384, 32768, 65536), steps: int = 400):
     """Cost of the compact-pattern fit as T grows: the recipe's 400 Adam
     steps on n_heads heads whose targets are the marginals of uniform causal
@@ -317,11 +327,11 @@ def fit_scaling_leg(B, stream, n_heads: int = 12, Ts=(4096, 8192, 16384, 32768, 
 
     rows = []
     for T in Ts:
-        H = np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, T + 1, dtype=np.float64))])
-        eta = torch.from_numpy((H[T] - H[:T]).astype(np.float32)).cuda()
+        eta64, negent64 = uniform_causal_targets(T)
+        eta = torch.from_numpy(eta64.astype(np.float32)).cuda()
         eta_abs = eta.expand(n_heads, T).contiguous()
         eta_rel = eta_abs.clone()
-        negent = torch.full((n_heads,), -math.lgamma(T + 1.0), dtype=torch.float32, device="cuda")
+        negent = torch.full((n_heads,), negent64, dtype=torch.float32, device="cuda")
         ws = torch.empty(max(B.fit_pattern_workspace_bytes(n_heads, T), 256), dtype=torch.uint8, device="cuda")
 
         def fit(J):

@@ -67,6 +67,22 @@ def test_calibration_flop_accounting():
     assert bench.CALIB_FLOPS_PER_UPDATE == 8
 
 
+def test_fit_scaling_targets_closed_form():
+    # the fit T-scaling leg's targets equal the oracle's statistics of a
+    # uniform causal mean (column sums, diagonal sums, sum P ln P)
+    import numpy as np
+
+    from oracle.saf_fit_oracle import fit_statistics
+
+    for T in (1, 7, 64):
+        A = np.tril(np.ones((T, T))) / np.arange(1, T + 1)[:, None]
+        st = fit_statistics(A)
+        eta, negent = bench.uniform_causal_targets(T)
+        np.testing.assert_allclose(eta, st["eta_abs"], rtol=1e-12, atol=0)
+        np.testing.assert_allclose(eta, st["eta_rel"], rtol=1e-12, atol=0)
+        assert abs(negent - st["negent"]) <= 1e-10 * max(1.0, abs(negent))
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
