@@ -626,8 +626,6 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
   }
   dl += xor32(dl);
   if (hl == 0 && i < T) A.delta[rowv] = dl;
-  // (delta is subtracted in the softmax step: seeding the dP accumulators
-  // with it would keep 16 more registers live and spill at 3 waves per SIMD)
 
   const int last_key = min(q0 + kQBM, T) - 1;
   const int ntiles = last_key / kQBN + 1;
@@ -646,6 +644,15 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db) dqa[db] = f32x16{};
   const float sl2 = A.scale_log2;
+  // d = 64: the tile's two 32-key halves are computed in sequence, which
+  // leaves room for -delta in 16 registers, the C operand of each half's
+  // first dP product, so that the accumulator arrives as dP - delta (one
+  // subtraction fewer per score).  Larger d computes both halves at once
+  // and subtracts delta in the softmax step (a seed would spill there).
+  constexpr bool SEQ = D == 64;
+  f32x16 ndl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndl[r] = -dl;
 
   // One key tile.  MASK only for the tiles that reach the diagonal.
   auto tile = [&](int t, auto mask_tag) {
@@ -658,7 +665,37 @@ __global__ __launch_bounds__(kThreads, (D == 64 ? 3 : 1)) void bwd_q_kernel(BwdA
     }
     const lds_bf16* K = smem + (t & 1) * C::TILE;
     const lds_bf16* V = smem + (2 + (t & 1)) * C::TILE;
-    if (!MASK || j0 <= wq_hi) {
+    const bool live = !MASK || j0 <= wq_hi;
+    if constexpr (SEQ) {
+      if (live) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          f32x16 s = f32x16{}, dp = ndl;
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            s = mfma32(lds_frag_nat<D>(K, 32 * c, 16 * ks), qf[ks], s);
+            dp = mfma32(lds_frag_nat<D>(V, 32 * c, 16 * ks), of[ks], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(fmaf(s[r], sl2, -l2));
+            if constexpr (MASK) {
+              const int jj = j0 + 32 * c + 8 * (r >> 2) + 4 * hl + (r & 3);
+              if (jj > i) p = 0.f;
+            }
+            dp[r] = p * dp[r];
+          }
+          // dQ^T += K^T dS^T over this half's 32 keys
+#pragma unroll
+          for (int st = 2 * c; st < 2 * c + 2; ++st) {
+            const bf16x8 sf = pack_acc8(dp, 8 * (st & 1));
+#pragma unroll
+            for (int db = 0; db < C::NDB; ++db)
+              dqa[db] = mfma32(lds_frag_tr<D>(K, 16 * st, 32 * db), sf, dqa[db]);
+          }
+        }
+      }
+    } else if (live) {
       f32x16 s[2], dp[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
