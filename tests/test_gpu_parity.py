@@ -459,6 +459,10 @@ def test_gqa_forward_head_dims(B, D):
 def test_gqa_forward_fp32_and_strided(B):
     run_gqa_fwd_parity(B, CONFIGS["tiny"].with_(H=8, kv_heads=4, T=70, B=2, frozen=(1, 6), bwd=False,
                                                name="gqa_fp32"))
+    # d = 96 and 128: the fp32 rows are split over thread pairs
+    for D in (96, 128):
+        run_gqa_fwd_parity(B, CONFIGS["tiny"].with_(D=D, H=8, kv_heads=2, T=133, B=2, frozen=(0, 5),
+                                                   bwd=False, name=f"gqa_fp32_D{D}"))
     run_gqa_fwd_parity(B, CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, B=2, T=200, prior_len=None,
                                                             frozen=(0, 5), bwd=False, name="gqa_strided"),
                        strided=True)
