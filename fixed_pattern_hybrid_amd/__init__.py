@@ -8,7 +8,7 @@ built library -- there is no CPU fallback.
 
 import importlib
 
-__all__ = ["binding", "build"]
+__all__ = ["autograd", "binding", "build"]
 
 
 def __getattr__(name):
