@@ -58,5 +58,13 @@ class HybridAttentionFn(torch.autograd.Function):
 def hybrid_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: torch.Tensor, r: torch.Tensor,
                      frozen: Sequence[int], softmax_scale: Optional[float] = None) -> torch.Tensor:
     """O of the hybrid layer, differentiable in q, k, v and (for the frozen
-    heads) a and r.  frozen: length-H sequence of 0/1."""
-    return HybridAttentionFn.apply(q, k, v, a, r, frozen, softmax_scale)
+    heads) a and r.  frozen: length-H sequence of 0/1.
+
+    Under bf16 autocast on the GPU, q, k and v are cast to bf16 (the bf16
+    path; their gradients flow back through the cast) while a and r stay
+    fp32; other autocast dtypes leave the inputs as given (the library has
+    bf16 and fp32 paths only)."""
+    if torch.is_autocast_enabled("cuda") and torch.get_autocast_dtype("cuda") == torch.bfloat16:
+        q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    with torch.autocast("cuda", enabled=False):
+        return HybridAttentionFn.apply(q, k, v, a, r, frozen, softmax_scale)

@@ -90,6 +90,28 @@ def test_pattern_gradients_only(B, AG):
             assert not a.grad[h].any() and not r.grad[h].any()
 
 
+def test_bf16_autocast(B, AG):
+    # fp32 q, k, v under bf16 autocast run the bf16 path; their gradients are
+    # those of the bf16 call, cast back to fp32
+    cfg = CONFIGS["tiny"].with_(B=2, T=129, H=4, frozen=(1, 3), prior_len=192, name="autograd_autocast")
+    inp = make_inputs(cfg, with_do=True)
+    dev = upload(inp)  # fp32 tensors
+    fz = [int(x) for x in inp.frozen]
+    q, k, v = (_leaf(dev[n], True) for n in ("q", "k", "v"))
+    with torch.autocast("cuda", dtype=torch.bfloat16):
+        O = AG.hybrid_attention(q, k, v, dev["a"], dev["r"], fz)
+    assert O.dtype == torch.bfloat16
+    g = dev["do"].to(torch.bfloat16)
+    O.backward(g)
+    qb, kb_, vb = (dev[n].to(torch.bfloat16) for n in ("q", "k", "v"))
+    O2, L2 = B.saf_hybrid_attn_fwd(qb, kb_, vb, fz, dev["a"], dev["r"])
+    dq, dk, dv = B.saf_hybrid_attn_bwd(qb, kb_, vb, O2, g, L2, fz, dev["a"], dev["r"])
+    torch.cuda.synchronize()
+    assert torch.equal(O.detach(), O2)
+    for got, want in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
+        assert got.dtype == torch.float32 and torch.equal(got, want.float())
+
+
 def test_grouped_query_backward_is_refused(B, AG):
     cfg = CONFIGS["pages_check_t129"].with_(H=8, kv_heads=2, B=1, T=64, prior_len=None, frozen=(1,),
                                             name="autograd_gqa")
