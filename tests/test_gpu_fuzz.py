@@ -8,8 +8,12 @@ head dimension, dtype, frozen mask, stored prior length, tensor strides
 key/value heads (forward only), the caller's stored log N, an explicit
 softmax scale and the pattern gradients.  Each operation is compared with
 the oracle at the layer's parity bars; the test stops at the first failure
-and names the operation.
+and names the operation.  More seeds on request: SAF_FUZZ_SEEDS=7,99,2026
+(and SAF_FUZZ_OPS, default 150) runs that many operations per seed in
+test_fuzz_more_seeds, which is skipped otherwise.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -176,3 +180,17 @@ def test_fuzz_50_operations(B):
             run_op(B, op)
         except AssertionError as e:
             raise AssertionError(f"fuzz operation {op['idx']} failed: {op}: {e}") from e
+
+
+def test_fuzz_more_seeds(B):
+    seeds = [int(x) for x in os.environ.get("SAF_FUZZ_SEEDS", "").split(",") if x.strip()]
+    if not seeds:
+        pytest.skip("set SAF_FUZZ_SEEDS to fuzz with more generator seeds")
+    n = int(os.environ.get("SAF_FUZZ_OPS", "150"))
+    for seed in seeds:
+        for op in draw_ops(n=n, seed=seed):
+            say(f"fuzz seed {seed} op {op['idx']}: {op}")
+            try:
+                run_op(B, op)
+            except AssertionError as e:
+                raise AssertionError(f"fuzz seed {seed} operation {op['idx']} failed: {op}: {e}") from e
