@@ -182,6 +182,7 @@ def test_fuzz_50_operations(B):
             raise AssertionError(f"fuzz operation {op['idx']} failed: {op}: {e}") from e
 
 
+@pytest.mark.gpu
 def test_fuzz_more_seeds(B):
     seeds = [int(x) for x in os.environ.get("SAF_FUZZ_SEEDS", "").split(",") if x.strip()]
     if not seeds:
